@@ -1,0 +1,76 @@
+"""CPU oracle for row-wise top-k selection -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The library under test never
+does, and it shares no code with it.
+
+The oracle is ``oracle.c``: a per-row full sort under the strict total order
+"larger value first; +0 before -0; lower index first among equal values",
+taking the first k (see the header of ``oracle.c`` for the readings).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, BAD_ARG, NAN, NOMEM = 0, 1, 4, 6
+_DT = {"bf16": 0, "f32": 1}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain C, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_topk.restype = ctypes.c_int
+        lib.oracle_topk.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: bool = True,
+         return_value: bool = True, nthreads: int = 1
+         ) -> Tuple[int, np.ndarray, Optional[np.ndarray]]:
+    """Top-k of each row of ``raw`` ([batch, row_stride] raw element bits:
+    uint16 for bf16, float32 for fp32).  Returns (status, indices int32
+    [batch, k], values [batch, k] of raw's dtype or None)."""
+    lib = _load()
+    raw = np.ascontiguousarray(raw)
+    want = np.uint16 if dtype == "bf16" else np.float32
+    if raw.dtype != want:
+        raise TypeError("raw must be %s for %s" % (np.dtype(want).name, dtype))
+    batch, row_stride = raw.shape
+    idx = np.zeros((batch, k), dtype=np.int32)
+    val = np.zeros((batch, k), dtype=want) if return_value else None
+    st = lib.oracle_topk(raw.ctypes.data, _DT[dtype], batch, n, row_stride, k,
+                         int(bool(sorted_index)), int(bool(return_value)), idx.ctypes.data,
+                         val.ctypes.data if val is not None else None, int(nthreads))
+    return st, idx, val

@@ -1,0 +1,240 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * brute-force rank counting (pure Python loops, and a numpy broadcast form);
+  * closed forms: strictly ascending rows, constant rows, k = n, rows whose
+    valid prefix is shorter than k (-inf tail), quantised ascending levels;
+  * a library cross-check (numpy argpartition) on rows without ties;
+  * the O(n) completeness invariant at the full workload sizes;
+  * bit-exact values, ascending sorted indices, NaN status, argument errors;
+  * planted mistakes: mutated copies of oracle.c must fail these pins.
+"""
+
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from brute import topk_set_loop, topk_set_numpy
+from invariants import check_topk_row, check_values_row
+from workloads import CONFIGS, bf16_bits_from_f32, make_edge_rows, make_workload
+
+DTYPES = ["bf16", "f32"]
+
+
+def _oracle_set(oracle_mod, raw, dtype, n, k):
+    st, idx, _ = oracle_mod.topk(raw, dtype, n, k, sorted_index=True, return_value=False)
+    assert st == oracle_mod.OK
+    return idx
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_brute_loop_tiny_every_k(oracle_mod, dtype):
+    # Tiny rows with heavy ties, +-0, +-inf, denormals; every k in 1..n.
+    for seed in range(40):
+        n = 1 + seed % 23
+        raw = make_edge_rows(dtype, 1, n, seed=seed, levels=3 + seed % 4, specials=0.3)
+        for k in range(1, n + 1):
+            got = _oracle_set(oracle_mod, raw, dtype, n, k)[0]
+            want = topk_set_loop(raw[0, :n], dtype, k)
+            assert got.tolist() == want, (seed, n, k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_brute_numpy_medium(oracle_mod, dtype):
+    rng = np.random.default_rng(123)
+    for seed in range(12):
+        n = int(rng.integers(50, 2049))
+        k = int(rng.integers(1, min(n, 4096) + 1))
+        raw = make_edge_rows(dtype, 2, n, seed=100 + seed, levels=[0, 5, 40][seed % 3],
+                             specials=[0.0, 0.05, 0.5][seed % 3])
+        got = _oracle_set(oracle_mod, raw, dtype, n, k)
+        for r in range(2):
+            want = topk_set_numpy(raw[r, :n], dtype, k)
+            assert got[r].tolist() == want.tolist(), (seed, n, k, r)
+
+
+def test_brute_forms_agree():
+    # The two brute-force forms must agree with each other.
+    raw = make_edge_rows("bf16", 3, 30, seed=7, levels=4, specials=0.4)
+    for r in range(3):
+        for k in (1, 5, 17, 30):
+            assert topk_set_loop(raw[r, :30], "bf16", k) == topk_set_numpy(raw[r, :30], "bf16", k).tolist()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_closed_form_ascending(oracle_mod, dtype):
+    # Strictly ascending distinct values: the top-k is the last k columns.
+    n, k = 1000, 77
+    if dtype == "bf16":
+        neg = np.arange(0xBF80 + n // 2 - 1, 0xBF80 - 1, -1)  # -big ... -1.0
+        pos = np.arange(0x3F80, 0x3F80 + n - n // 2)         # +1.0 ... +big
+        raw = np.concatenate([neg, pos]).astype(np.uint16)[None]
+    else:
+        raw = np.linspace(-50, 50, n).astype(np.float32)[None]
+        assert np.all(np.diff(raw[0]) > 0)
+    got = _oracle_set(oracle_mod, raw, dtype, n, k)[0]
+    assert got.tolist() == list(range(n - k, n))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_closed_form_constant(oracle_mod, dtype):
+    n = 513
+    for v in (1.5, 0.0, -0.0, float("inf"), float("-inf")):
+        raw = (bf16_bits_from_f32(np.full(n, v, np.float32))[None] if dtype == "bf16"
+               else np.full((1, n), v, np.float32))
+        for k in (1, 64, n):
+            got = _oracle_set(oracle_mod, raw, dtype, n, k)[0]
+            assert got.tolist() == list(range(k)), (v, k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_closed_form_k_equals_n(oracle_mod, dtype):
+    raw = make_edge_rows(dtype, 3, 257, seed=9, specials=0.2)
+    st, idx, val = oracle_mod.topk(raw, dtype, 257, 257, sorted_index=True, return_value=True)
+    assert st == 0
+    for r in range(3):
+        assert idx[r].tolist() == list(range(257))
+        check_values_row(raw[r], idx[r], val[r])
+
+
+def test_closed_form_short_valid_prefix(oracle_mod):
+    # A valid prefix of length L < k followed by -inf: the answer is {0..k-1}
+    # (all L valid entries, then the lowest-index -inf entries).
+    n, k = 4096, 512
+    rng = np.random.default_rng(5)
+    for L in (1, 100, 511, 512):
+        row = bf16_bits_from_f32(rng.standard_normal(n).astype(np.float32))
+        row[L:] = 0xFF80
+        got = _oracle_set(oracle_mod, row[None], "bf16", n, k)[0]
+        assert got.tolist() == list(range(k)), L
+
+
+def c5_closed_form(level_counts, k):
+    """Top-k of a row of ascending quantised levels, ties to lower index."""
+    counts = np.asarray(level_counts)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    above = 0
+    for lvl in range(len(counts) - 1, -1, -1):
+        if above + counts[lvl] >= k:
+            take = k - above
+            tied = np.arange(starts[lvl], starts[lvl] + take)
+            rest = np.arange(starts[lvl] + counts[lvl], counts.sum())
+            return np.concatenate([tied, rest])
+        above += counts[lvl]
+    raise AssertionError
+
+
+def test_closed_form_quantised_ascending(oracle_mod):
+    w = make_workload("C5", batch=16)
+    st, idx, val = oracle_mod.topk(w.raw, "bf16", w.n, w.k, True, True, nthreads=0)
+    assert st == 0
+    for r in range(w.batch):
+        assert idx[r].tolist() == c5_closed_form(w.meta["level_counts"][r], w.k).tolist()
+        check_values_row(w.raw[r], idx[r], val[r])
+
+
+def test_library_crosscheck_no_ties(oracle_mod):
+    # Distinct fp32 values in shuffled order: no ties, so numpy's
+    # argpartition gives the same set.
+    rng = np.random.default_rng(11)
+    x = ((rng.permuted(np.tile(np.arange(20000), (8, 1)), axis=1) - 10000) * 0.5).astype(np.float32)
+    assert all(np.unique(r).size == r.size for r in x)
+    for k in (1, 100, 4096):
+        got = _oracle_set(oracle_mod, x, "f32", 20000, k)
+        for r in range(8):
+            want = np.sort(np.argpartition(-x[r].astype(np.float64), k - 1)[:k])
+            assert got[r].tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("cfg", sorted(CONFIGS))
+def test_full_workloads_invariant(oracle_mod, cfg):
+    w = make_workload(cfg)
+    st, idx, val = oracle_mod.topk(w.raw, w.dtype, w.n, w.k, w.sorted_index, True, nthreads=0)
+    assert st == 0
+    rows = range(w.batch) if w.batch <= 8 else range(0, w.batch, max(1, w.batch // 8))
+    for r in rows:
+        check_topk_row(w.raw[r], w.dtype, w.n, w.k, idx[r], sorted_index=w.sorted_index)
+        check_values_row(w.raw[r], idx[r], val[r])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_nan_status(oracle_mod, dtype):
+    n = 100
+    raw = make_edge_rows(dtype, 3, n, seed=1, row_stride=104)
+    # padding (columns n..row_stride) already holds NaN: must be ignored
+    st, _, _ = oracle_mod.topk(raw, dtype, n, 10)
+    assert st == oracle_mod.OK
+    nan_bits = [0x7FC0, 0xFFC0, 0x7F81, 0xFF81] if dtype == "bf16" else [
+        np.uint32(0x7FC00000).view(np.float32), np.uint32(0xFFC00000).view(np.float32),
+        np.uint32(0x7F800001).view(np.float32), np.uint32(0xFF800001).view(np.float32)]
+    for b in nan_bits:
+        for col in (0, n // 2, n - 1):
+            bad = raw.copy()
+            bad[2, col] = b
+            st, _, _ = oracle_mod.topk(bad, dtype, n, 10)
+            assert st == oracle_mod.NAN, (repr(b), col)
+
+
+def test_bad_args(oracle_mod):
+    raw = make_edge_rows("f32", 2, 16, seed=0)
+    assert oracle_mod.topk(raw, "f32", 16, 0)[0] == oracle_mod.BAD_ARG
+    assert oracle_mod.topk(raw, "f32", 16, 17)[0] == oracle_mod.BAD_ARG
+    assert oracle_mod.topk(raw, "f32", 17, 4)[0] == oracle_mod.BAD_ARG  # row_stride < n
+
+
+def test_unsorted_is_rank_order(oracle_mod):
+    raw = make_edge_rows("bf16", 1, 300, seed=3, levels=6)
+    st, a, _ = oracle_mod.topk(raw, "bf16", 300, 40, sorted_index=True)
+    st2, b, _ = oracle_mod.topk(raw, "bf16", 300, 40, sorted_index=False)
+    assert st == st2 == 0
+    assert sorted(b[0].tolist()) == a[0].tolist()
+
+
+# ---------------------------------------------------------------- planted mistakes
+_MUTANTS = {
+    "tie_to_higher_index": ("if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
+                            "if (a->i > b->i) return -1;\n    if (a->i < b->i) return 1;"),
+    "zero_sign_reversed": ("return sa ? 1 : -1;", "return sa ? -1 : 1;"),
+    "drops_last_column": ("for (int64_t c = 0; c < n; ++c) {", "for (int64_t c = 0; c < n - 1; ++c) {"),
+    "bf16_low_half": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;"),
+    "no_nan_check": ("if (isnan(it[c].v)) {", "if (0) {"),
+}
+
+
+def _build_mutant(name):
+    src = open(os.path.join(os.path.dirname(__file__), "..", "oracle", "oracle.c")).read()
+    old, new = _MUTANTS[name]
+    assert old in src, name
+    d = tempfile.mkdtemp()
+    cpath, so = os.path.join(d, "m.c"), os.path.join(d, "libm.so")
+    open(cpath, "w").write(src.replace(old, new))
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", so, cpath, "-lm"])
+    return so
+
+
+def _pins_pass(oracle_mod):
+    try:
+        test_brute_loop_tiny_every_k(oracle_mod, "bf16")
+        test_brute_loop_tiny_every_k(oracle_mod, "f32")
+        test_closed_form_ascending(oracle_mod, "bf16")
+        test_closed_form_constant(oracle_mod, "bf16")
+        test_nan_status(oracle_mod, "bf16")
+        test_nan_status(oracle_mod, "f32")
+    except AssertionError:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_mistake_is_caught(oracle_mod, name, monkeypatch):
+    import ctypes
+
+    so = _build_mutant(name)
+    lib = ctypes.CDLL(so)
+    lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = oracle_mod._load().oracle_topk.argtypes
+    monkeypatch.setattr(oracle_mod, "_lib", lib)
+    assert not _pins_pass(oracle_mod), "pins did not catch mutant %s" % name
