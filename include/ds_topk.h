@@ -1,0 +1,171 @@
+/*
+ * ds_topk -- row-wise small-k top-k selection on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Device buffers are HIP device
+ * memory of the current device; `stream` is a hipStream_t (NULL = the null
+ * stream).
+ *
+ * The operation (CSDN page "DeepSeek 一次开源三个仓库", section 三 算子层:
+ * a top-k operator for sparse-attention indexing and for sampling, small k
+ * only, at most 4096; usage `values, indices = deep_select.topk(x, topk,
+ * sorted_index=..., indices_type=torch.int32)`):
+ *
+ *   For every row r of a [batch][row_stride] matrix, select the k largest of
+ *   the elements in columns [0, n) and return their column indices (int32)
+ *   and, optionally, their values.
+ *
+ *   "Largest" is a strict total order: element i comes before element j iff
+ *   its value is larger, or both are zeros and i is +0 while j is -0, or the
+ *   two values are the same and i < j (the lower index wins a tie).  +inf is
+ *   largest and -inf smallest; they are ordinary values.  The answer is
+ *   therefore unique for every input without NaN.
+ *
+ * Scenarios (aiutil project card "deepseek-ai/DeepSelect", 关键技术亮点
+ * item 1): bf16 scores with any batch and length (the sparse-attention
+ * "Lightning Indexer"), fp32 logits with a vocabulary of about 128K (the
+ * sampler); k <= 4096 for both.  One library call serves both; the plan
+ * (one workgroup per row, or several per row plus a merge) is chosen from
+ * dtype, batch, n and k.
+ */
+#ifndef DS_TOPK_H
+#define DS_TOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (aiutil card, 关键技术亮点 item 1; no other dtype). */
+enum ds_topk_dtype {
+    DS_DTYPE_BF16 = 0, /* bfloat16: the upper 16 bits of an IEEE binary32 */
+    DS_DTYPE_F32 = 1   /* IEEE binary32 */
+};
+
+/* Status codes returned by every entry point. */
+enum ds_topk_status {
+    DS_OK = 0,
+    /* A null `in` or `out_idx`; `return_value` set with a null `out_val`;
+       batch < 0; n < 1; k < 1; k > n; row_stride < n. */
+    DS_ERR_INVALID_ARGUMENT = 1,
+    /* k > 4096 (CSDN page, section 三: small top-k only, at most 4096);
+       an unknown dtype; n > 2^31 - 1 (indices are int32). */
+    DS_ERR_UNSUPPORTED = 2,
+    /* `in` not 16-byte aligned, or row_stride * element size not a multiple
+       of 16 bytes.  The pages say input rows need a specific alignment and
+       callers may need to pad them (zh-TW page "深入 DeepSeek V4.1
+       全新開放推論工具包", section DeepSelect); here: pad each row to a
+       multiple of 8 bf16 / 4 fp32 elements. */
+    DS_ERR_MISALIGNED = 3,
+    /* Some row holds a NaN (either sign, any payload) in columns [0, n).
+       The pages: NaN checking is always on, and their default traps and
+       aborts (same zh-TW page and section); this library reports it
+       instead.  Outputs are unspecified.  Padding columns are never
+       examined. */
+    DS_ERR_NAN = 4,
+    /* A HIP runtime call failed; ds_topk_last_error() has the detail. */
+    DS_ERR_HIP = 5
+};
+
+#define DS_TOPK_MAX_K 4096
+
+/*
+ * ds_topk: top-k of every row, synchronous.
+ *
+ *   in           device pointer to batch * row_stride elements of `dtype`,
+ *                row r at element offset r * row_stride, 16-byte aligned.
+ *                Columns [n, row_stride) are padding: never used for results
+ *                or NaN checks (they may be read, up to the next 16-byte
+ *                boundary after column n - 1).
+ *   dtype        DS_DTYPE_BF16 or DS_DTYPE_F32.
+ *   batch        number of rows, >= 0 (0 is a no-op returning DS_OK).
+ *   n            valid columns per row, 1 <= n <= 2^31 - 1.
+ *   row_stride   elements between row starts, >= n; row_stride * element
+ *                size must be a multiple of 16 bytes.
+ *   k            1 <= k <= min(n, 4096).
+ *   sorted_index nonzero: each row's k indices are written in ascending
+ *                order (aiutil card, 关键技术亮点 item 2: sorted output costs
+ *                speed, so leave it off unless needed).  Zero: the order
+ *                within a row is unspecified and may differ between calls;
+ *                the set is always the same.
+ *   return_value nonzero: write the selected values to out_val.  Zero: skip
+ *                that output (zh-TW page, section DeepSelect:
+ *                return_value=False skips the values and is faster).
+ *   out_idx      device pointer, [batch][k] int32, contiguous: column
+ *                indices in [0, n).
+ *   out_val      device pointer, [batch][k] elements of `dtype`, contiguous;
+ *                out_val[r][j] is a bit-exact copy of in[r][out_idx[r][j]]
+ *                (-0, -inf and every bf16 bit pattern are kept).  May be
+ *                NULL when return_value is zero.
+ *   stream       hipStream_t the work is enqueued on.
+ *
+ * Ownership: the caller owns in, out_idx, out_val and the stream.  The
+ * library owns a per-(device, stream) workspace that it allocates on first
+ * use, grows when a larger call needs it (growing synchronises the device)
+ * and keeps until the process exits.
+ *
+ * Synchronisation: the call enqueues the kernel(s) on `stream`, then waits
+ * for the stream so that it can return DS_ERR_NAN; when it returns, the
+ * outputs are complete.  Argument errors are returned before any HIP call,
+ * and nothing is written.  Calls on different streams may run concurrently;
+ * they use different workspaces.
+ */
+int ds_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+            int sorted_index, int return_value, int32_t* out_idx, void* out_val, void* stream);
+
+/*
+ * ds_topk_async: the same selection, enqueued without waiting.
+ *
+ * Arguments are those of ds_topk, plus `status_dev`: a device pointer to one
+ * int32 that the caller has set to 0 (DS_OK).  If any row holds a NaN, the
+ * kernels store DS_ERR_NAN there; they never store anything else, so one
+ * status word can collect several calls.  The return value reports argument
+ * and launch errors only.  Work on `stream` is ordered as usual; the
+ * workspace rules of ds_topk apply (calls on one stream may be queued back to
+ * back).
+ */
+int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
+                  int32_t k, int sorted_index, int return_value, int32_t* out_idx, void* out_val,
+                  int32_t* status_dev, void* stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* ds_topk_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* ds_topk_last_error(void);
+
+/*
+ * The launch plan ds_topk would use for these arguments, without touching
+ * the GPU.  Validates exactly like ds_topk (same status codes, except that
+ * the pointer checks are skipped).
+ */
+typedef struct ds_topk_plan {
+    int32_t segments;        /* workgroups per row; > 1 means split rows + merge */
+    int32_t threads;         /* threads per workgroup */
+    int32_t vectors_per_tile_thread; /* 16-byte loads per thread per tile */
+    int32_t capacity;        /* candidate-buffer entries per workgroup (LDS) */
+    int32_t segment_vectors; /* 16-byte vectors per segment (last may be shorter) */
+    int32_t tiles_per_segment;
+    int64_t grid;            /* workgroups launched */
+    int64_t workspace_bytes; /* device workspace this call needs */
+} ds_topk_plan;
+
+int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                     int sorted_index, int return_value, ds_topk_plan* plan);
+
+/*
+ * Tuning overrides, process-wide (for tests and measurements):
+ * segments > 0 forces that many workgroups per row (clamped to what the row
+ * length allows); 0 restores the automatic choice.  tile_seed changes the
+ * pseudo-random tile visiting order (the result never depends on it).
+ */
+void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ds_topk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_TOPK_H */

@@ -1,0 +1,341 @@
+// Host side of the ds_topk C ABI: argument checks, launch planning,
+// per-(device, stream) workspace, kernel launch and NaN status readback.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "ds_topk.h"
+#include "topk_kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;       // 0.1.0
+constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS count each)
+constexpr int kTargetWG = 512;      // about two workgroups per CU on a 256-CU MI355X
+constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
+constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+std::atomic<int32_t> g_force_segs{0};
+std::atomic<uint32_t> g_tile_seed{0x2545F491u};
+
+struct Plan {
+    int eb = 0;    // element bytes
+    int wg = 512;  // threads per workgroup
+    int vpt = 1;   // 16-byte loads per thread per tile
+    int cap = 0;   // LDS candidate capacity
+    int segs = 1;
+    int seg_vecs = 0;
+    int n_vec = 0;
+    int tiles = 0;
+    int idx_bits = 0;
+    int64_t rows_per_launch = 0;
+    int64_t ws_bytes = 0;
+};
+
+int validate(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k) {
+    if (dtype != DS_DTYPE_BF16 && dtype != DS_DTYPE_F32)
+        return fail(DS_ERR_UNSUPPORTED, "dtype %d is neither DS_DTYPE_BF16 nor DS_DTYPE_F32", dtype);
+    if (batch < 0) return fail(DS_ERR_INVALID_ARGUMENT, "batch %lld < 0", (long long)batch);
+    if (n < 1) return fail(DS_ERR_INVALID_ARGUMENT, "n %lld < 1", (long long)n);
+    if (k < 1) return fail(DS_ERR_INVALID_ARGUMENT, "k %d < 1", k);
+    if (n > 0x7FFFFFFFLL) return fail(DS_ERR_UNSUPPORTED, "n %lld exceeds the int32 index range", (long long)n);
+    if (k > DS_TOPK_MAX_K) return fail(DS_ERR_UNSUPPORTED, "k %d > %d", k, DS_TOPK_MAX_K);
+    if (k > n) return fail(DS_ERR_INVALID_ARGUMENT, "k %d > n %lld", k, (long long)n);
+    if (row_stride < n)
+        return fail(DS_ERR_INVALID_ARGUMENT, "row_stride %lld < n %lld", (long long)row_stride, (long long)n);
+    const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
+    if ((row_stride * es) % 16 != 0)
+        return fail(DS_ERR_MISALIGNED, "row pitch %lld bytes is not a multiple of 16", (long long)(row_stride * es));
+    return DS_OK;
+}
+
+int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
+    pl->eb = dtype == DS_DTYPE_BF16 ? 2 : 4;
+    const int epv = 16 / pl->eb;
+    pl->wg = 512;
+    if (pl->eb == 2) {
+        pl->vpt = k <= 1024 ? 1 : 2;
+        pl->cap = k <= 1024 ? 8192 : 16384;
+    } else {
+        pl->vpt = 2;
+        pl->cap = k <= 1024 ? 8192 : 16384;
+    }
+    const int tile_vecs = pl->wg * pl->vpt;
+    pl->n_vec = (int)((n + epv - 1) / epv);
+    int64_t s;
+    const int32_t forced = g_force_segs.load();
+    if (forced > 0) {
+        s = forced;
+    } else {
+        s = batch >= kTargetWG ? 1 : (kTargetWG + batch - 1) / (batch > 0 ? batch : 1);
+        const int64_t by_k = n / ((int64_t)kSegPerK * k);
+        if (s > by_k) s = by_k;
+    }
+    if (s > kMaxSegs) s = kMaxSegs;
+    if (s > pl->n_vec) s = pl->n_vec;
+    if (s < 1) s = 1;
+    pl->seg_vecs = (int)((pl->n_vec + s - 1) / s);
+    pl->segs = (pl->n_vec + pl->seg_vecs - 1) / pl->seg_vecs;
+    pl->tiles = (pl->seg_vecs + tile_vecs - 1) / tile_vecs;
+    pl->idx_bits = n <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n - 1));
+    const int64_t max_rows = kMaxGridWG / pl->segs;
+    pl->rows_per_launch = batch < max_rows ? batch : max_rows;
+    const int64_t r = pl->rows_per_launch;
+    pl->ws_bytes = 256 + 256;  // NaN word
+    if (pl->segs > 1) {
+        pl->ws_bytes += ((r * 4 + 255) / 256) * 256;                          // tickets
+        pl->ws_bytes += ((r * pl->segs * 4 + 255) / 256) * 256;               // counts
+        pl->ws_bytes += ((r * pl->segs * 8 + 255) / 256) * 256;               // k-th keys
+        pl->ws_bytes += ((r * pl->segs * (int64_t)k * 8 + 255) / 256) * 256;  // candidates
+    }
+    return DS_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+struct Workspace {
+    std::mutex mu;
+    int device = -1;
+    uint8_t* base = nullptr;
+    int64_t rows = 0, slots = 0, cands = 0;
+    int32_t* nan_word = nullptr;
+    uint32_t* ticket = nullptr;
+    uint32_t* count = nullptr;
+    uint64_t* kth = nullptr;
+    uint64_t* cand = nullptr;
+    int32_t* host_word = nullptr;  // pinned
+    int32_t epoch = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Workspace>> g_ws;
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Make sure ws can hold `rows` rows of `segs` segments of k entries.
+int ensure(Workspace* ws, int64_t rows, int segs, int32_t k) {
+    const int64_t need_rows = segs > 1 ? rows : 0;
+    const int64_t need_slots = segs > 1 ? rows * segs : 0;
+    const int64_t need_cands = segs > 1 ? rows * segs * (int64_t)k : 0;
+    if (ws->base && need_rows <= ws->rows && need_slots <= ws->slots && need_cands <= ws->cands) return DS_OK;
+    hipError_t e;
+    if (!ws->host_word) {
+        e = hipHostMalloc((void**)&ws->host_word, sizeof(int32_t), hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    }
+    const int64_t rows2 = need_rows > ws->rows ? need_rows : ws->rows;
+    const int64_t slots2 = need_slots > ws->slots ? need_slots : ws->slots;
+    const int64_t cands2 = need_cands > ws->cands ? need_cands : ws->cands;
+    auto al = [](int64_t b) { return ((b + 255) / 256) * 256; };
+    const int64_t bytes = 256 + al(rows2 * 4) + al(slots2 * 4) + al(slots2 * 8) + al(cands2 * 8);
+    if (ws->base) {
+        // Earlier calls may still be queued on this stream: let them finish.
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        e = hipFree(ws->base);
+        ws->base = nullptr;
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    e = hipMalloc((void**)&ws->base, (size_t)bytes);
+    if (e != hipSuccess) {
+        ws->base = nullptr;
+        ws->rows = ws->slots = ws->cands = 0;
+        return hip_fail(e, "hipMalloc(workspace)");
+    }
+    e = hipMemset(ws->base, 0, (size_t)bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
+    uint8_t* p = ws->base;
+    ws->nan_word = (int32_t*)p;
+    p += 256;
+    ws->ticket = (uint32_t*)p;
+    p += al(rows2 * 4);
+    ws->count = (uint32_t*)p;
+    p += al(slots2 * 4);
+    ws->kth = (uint64_t*)p;
+    p += al(slots2 * 8);
+    ws->cand = (uint64_t*)p;
+    ws->rows = rows2;
+    ws->slots = slots2;
+    ws->cands = cands2;
+    ws->epoch = 0;
+    return DS_OK;
+}
+
+Workspace* workspace_for(int dev, hipStream_t s) {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    auto& slot = g_ws[std::make_pair(dev, s)];
+    if (!slot) {
+        slot.reset(new Workspace());
+        slot->device = dev;
+    }
+    return slot.get();
+}
+
+template <int EB, int WG, int VPT, int CAP>
+hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((dstk::topk_rows<EB, WG, VPT, CAP>), dim3((uint32_t)grid), dim3(WG), 0, s, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s) {
+    const int64_t grid = rows * pl.segs;
+    if (pl.eb == 2) {
+        if (pl.cap == 8192) return launch_one<2, 512, 1, 8192>(prm, grid, s);
+        return launch_one<2, 512, 2, 16384>(prm, grid, s);
+    }
+    if (pl.cap == 8192) return launch_one<4, 512, 2, 8192>(prm, grid, s);
+    return launch_one<4, 512, 2, 16384>(prm, grid, s);
+}
+
+int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+        int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream) {
+    g_err.clear();
+    int st = validate(dtype, batch, n, row_stride, k);
+    if (st) return st;
+    if (!in) return fail(DS_ERR_INVALID_ARGUMENT, "in is NULL");
+    if (!out_idx) return fail(DS_ERR_INVALID_ARGUMENT, "out_idx is NULL");
+    if (return_value && !out_val) return fail(DS_ERR_INVALID_ARGUMENT, "return_value set but out_val is NULL");
+    if (((uintptr_t)in) % 16 != 0) return fail(DS_ERR_MISALIGNED, "in is not 16-byte aligned");
+    if (batch == 0) return DS_OK;
+    Plan pl;
+    make_plan(dtype, batch, n, k, &pl);
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    Workspace* ws = workspace_for(dev, stream);
+    std::lock_guard<std::mutex> g(ws->mu);
+    st = ensure(ws, pl.rows_per_launch, pl.segs, k);
+    if (st) return st;
+
+    int32_t* flag = status_dev;
+    int32_t flag_value = DS_ERR_NAN;
+    if (!status_dev) {
+        if (ws->epoch >= 0x7FFFFFF0) {
+            e = hipMemsetAsync(ws->nan_word, 0, sizeof(int32_t), stream);
+            if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+            ws->epoch = 0;
+        }
+        flag = ws->nan_word;
+        flag_value = ++ws->epoch;
+    }
+
+    const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < batch; r0 += pl.rows_per_launch) {
+        const int64_t rows = batch - r0 < pl.rows_per_launch ? batch - r0 : pl.rows_per_launch;
+        dstk::Params prm;
+        prm.in = (const uint8_t*)in + r0 * row_stride * es;
+        prm.row_stride_bytes = row_stride * es;
+        prm.n = (int32_t)n;
+        prm.k = k;
+        prm.segs = pl.segs;
+        prm.seg_vecs = pl.seg_vecs;
+        prm.n_vec = pl.n_vec;
+        prm.idx_bits = pl.idx_bits;
+        prm.seed = g_tile_seed.load();
+        prm.sorted = sorted_index ? 1 : 0;
+        prm.retval = return_value ? 1 : 0;
+        prm.out_idx = out_idx + r0 * k;
+        prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
+        prm.ws_cand = ws->cand;
+        prm.ws_kth = ws->kth;
+        prm.ws_count = ws->count;
+        prm.ws_ticket = ws->ticket;
+        prm.flag = flag;
+        prm.flag_value = flag_value;
+        e = launch(pl, prm, rows, stream);
+        if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    }
+    if (status_dev) return DS_OK;
+
+    e = hipMemcpyAsync(ws->host_word, ws->nan_word, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (*ws->host_word == flag_value) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
+    return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ds_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+            int return_value, int32_t* out_idx, void* out_val, void* stream) {
+    return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, nullptr,
+               (hipStream_t)stream);
+}
+
+int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                  int sorted_index, int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev,
+                  void* stream) {
+    if (!status_dev) return fail(DS_ERR_INVALID_ARGUMENT, "status_dev is NULL");
+    return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, status_dev,
+               (hipStream_t)stream);
+}
+
+const char* ds_topk_status_string(int status) {
+    switch (status) {
+        case DS_OK: return "DS_OK: success";
+        case DS_ERR_INVALID_ARGUMENT: return "DS_ERR_INVALID_ARGUMENT: invalid argument";
+        case DS_ERR_UNSUPPORTED: return "DS_ERR_UNSUPPORTED: unsupported dtype, k or n";
+        case DS_ERR_MISALIGNED: return "DS_ERR_MISALIGNED: input or row pitch not 16-byte aligned";
+        case DS_ERR_NAN: return "DS_ERR_NAN: input holds NaN";
+        case DS_ERR_HIP: return "DS_ERR_HIP: HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* ds_topk_last_error(void) { return g_err.c_str(); }
+
+int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+                     int return_value, ds_topk_plan* plan) {
+    (void)sorted_index;
+    (void)return_value;
+    g_err.clear();
+    const int st = validate(dtype, batch, n, row_stride, k);
+    if (st) return st;
+    if (!plan) return fail(DS_ERR_INVALID_ARGUMENT, "plan is NULL");
+    Plan pl;
+    make_plan(dtype, batch, n, k, &pl);
+    plan->segments = pl.segs;
+    plan->threads = pl.wg;
+    plan->vectors_per_tile_thread = pl.vpt;
+    plan->capacity = pl.cap;
+    plan->segment_vectors = pl.seg_vecs;
+    plan->tiles_per_segment = pl.tiles;
+    plan->grid = pl.rows_per_launch * pl.segs;
+    plan->workspace_bytes = pl.ws_bytes;
+    return DS_OK;
+}
+
+void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed) {
+    g_force_segs.store(segments > 0 ? segments : 0);
+    g_tile_seed.store(tile_seed ? tile_seed : 0x2545F491u);
+}
+
+int ds_topk_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and its host-side checks and planning behave as documented.  None of these
+calls reaches the GPU (argument errors return before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds_topk.h")
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    from sampling_topk_selection_amd import build as b
+
+    b.build(force=False)
+    import sampling_topk_selection_amd as p
+
+    p.load_library()
+    return p
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds_topk\w*)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    assert "ds_topk" in fns and "ds_topk_status_string" in fns
+    assert len(fns) >= 5
+
+
+def test_library_exports_every_declared_symbol(pkg):
+    lib = ctypes.CDLL(pkg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), "missing export %s" % name
+    assert set(pkg.EXPORTS) == set(declared_functions())
+
+
+def test_binds_to_one_hip_runtime(pkg):
+    maps = open("/proc/self/maps").read()
+    libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(libs) == 1, libs
+
+
+def test_status_strings(pkg):
+    for st in range(6):
+        s = pkg.ds_topk_status_string(st)
+        assert s.startswith("DS_")
+    assert pkg.ds_topk_status_string(99) == "unknown status"
+    assert pkg.ds_topk_version() >= 100
+
+
+BF, F32 = 0, 1
+FAKE = 1 << 20  # never dereferenced: argument errors return first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((BF, 4, 100, 104, 0), 1),        # k < 1
+    ((BF, 4, 100, 104, 101), 1),      # k > n
+    ((BF, -1, 100, 104, 4), 1),       # batch < 0
+    ((BF, 4, 0, 8, 1), 1),            # n < 1
+    ((BF, 4, 100, 96, 4), 1),         # row_stride < n
+    ((BF, 4, 5000, 5000, 4097), 2),   # k > 4096
+    ((7, 4, 100, 104, 4), 2),         # dtype
+    ((BF, 4, 1 << 31, 1 << 31, 4), 2),  # n beyond int32
+    ((BF, 4, 100, 100, 4), 3),        # bf16 pitch 200 B
+    ((F32, 4, 100, 102, 4), 3),       # fp32 pitch 408 B
+])
+def test_validation_errors(pkg, args, status):
+    dtype, batch, n, rs, k = args
+    st = pkg.ds_topk(FAKE, dtype, batch, n, rs, k, 0, 0, FAKE, None, None)
+    assert st == status, pkg.ds_topk_last_error()
+    assert pkg.ds_topk_last_error()
+    st2, _ = pkg.ds_topk_plan_for(dtype, batch, n, rs, k)
+    assert st2 == status
+
+
+def test_pointer_errors(pkg):
+    assert pkg.ds_topk(None, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None) == 1
+    assert pkg.ds_topk(FAKE, BF, 4, 64, 64, 8, 0, 0, None, None, None) == 1
+    assert pkg.ds_topk(FAKE, BF, 4, 64, 64, 8, 0, 1, FAKE, None, None) == 1  # values wanted, no buffer
+    assert pkg.ds_topk(FAKE + 2, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None) == 3  # misaligned base
+    assert pkg.ds_topk_async(FAKE, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None, None) == 1  # no status word
+
+
+def test_k_limits_from_pages(pkg):
+    import json
+
+    lim = json.load(open(os.path.join(ROOT, "tests", "golden", "page_limits.json")))["k_max"]["value"]
+    assert pkg.ds_topk_plan_for(BF, 1, 8192, 8192, lim)[0] == 0
+    assert pkg.ds_topk_plan_for(BF, 1, 8192, 8192, lim + 1)[0] == 2
+
+
+def test_batch_zero_is_noop(pkg):
+    # valid arguments, zero rows: returns before any HIP call
+    assert pkg.ds_topk(FAKE, BF, 0, 64, 64, 8, 0, 0, FAKE, None, None) == 0
+
+
+@pytest.mark.parametrize("cfg", ["C1", "C2", "C3", "C4", "C5"])
+def test_plans_for_workloads(pkg, cfg):
+    from workloads import CONFIGS
+
+    c = CONFIGS[cfg]
+    dt = BF if c["dtype"] == "bf16" else F32
+    st, p = pkg.ds_topk_plan_for(dt, c["batch"], c["n"], c["n"], c["k"], int(c["sorted_index"]),
+                                 int(c["return_value"]))
+    assert st == 0
+    epv = 8 if dt == BF else 4
+    n_vec = -(-c["n"] // epv)
+    assert 1 <= p.segments <= 256
+    assert p.segments * p.segment_vectors >= n_vec > (p.segments - 1) * p.segment_vectors
+    assert p.capacity >= c["k"] + p.threads * p.vectors_per_tile_thread * epv
+    assert p.grid == c["batch"] * p.segments
+    if p.segments > 1:
+        assert p.workspace_bytes >= c["batch"] * p.segments * c["k"] * 8
+
+
+def test_forced_segments(pkg):
+    try:
+        pkg.ds_topk_set_overrides(7, 0)
+        st, p = pkg.ds_topk_plan_for(BF, 4, 204800, 204800, 1024)
+        assert st == 0 and p.segments == 7
+        pkg.ds_topk_set_overrides(100000, 0)
+        st, p = pkg.ds_topk_plan_for(BF, 4, 64, 64, 8)
+        assert st == 0 and p.segments == 8  # at most one segment per 16-byte vector
+    finally:
+        pkg.ds_topk_set_overrides(0, 0)

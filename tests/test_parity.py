@@ -1,0 +1,67 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+All five workloads at full size, under the automatic plan and with each row
+forced onto one workgroup and onto several (split + merge)."""
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_parity, gpu_topk, log
+from workloads import CONFIGS, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    import sampling_topk_selection_amd as p
+
+    p.load_library()
+    yield p
+    p.ds_topk_set_overrides(0, 0)
+
+
+def _oracle(oracle_mod, w, raw=None):
+    raw = w.raw if raw is None else raw
+    st, idx, val = oracle_mod.topk(raw, w.dtype, w.n, w.k, w.sorted_index, True, nthreads=0)
+    assert st == 0
+    return idx, val
+
+
+@pytest.mark.parametrize("cfg", sorted(CONFIGS))
+def test_workload_parity(pkg, oracle_mod, cfg):
+    w = make_workload(cfg)
+    st, plan = pkg.ds_topk_plan_for(0 if w.dtype == "bf16" else 1, w.batch, w.n, w.row_stride, w.k)
+    log("parity %s %s batch=%d n=%d k=%d segments=%d" % (cfg, w.dtype, w.batch, w.n, w.k, plan.segments))
+    gidx, gval = gpu_topk(w.raw, w.dtype, w.n, w.k, w.sorted_index, w.return_value)
+    oidx, oval = _oracle(oracle_mod, w)
+    assert_parity(w.raw, w.dtype, w.n, w.k, w.sorted_index, gidx, gval, oidx, oval,
+                  invariant_rows=range(0, w.batch, max(1, w.batch // 4)))
+
+
+@pytest.mark.parametrize("cfg", sorted(CONFIGS))
+@pytest.mark.parametrize("segs", [1, 3, 16])
+def test_workload_parity_forced_plan(pkg, oracle_mod, cfg, segs):
+    batch = min(CONFIGS[cfg]["batch"], 8)
+    w = make_workload(cfg, batch=batch)
+    log("forced plan %s segments=%d batch=%d" % (cfg, segs, batch))
+    pkg.ds_topk_set_overrides(segs, 0)
+    try:
+        for rv in (True, False):
+            gidx, gval = gpu_topk(w.raw, w.dtype, w.n, w.k, w.sorted_index, rv)
+            oidx, oval = _oracle(oracle_mod, w)
+            assert_parity(w.raw, w.dtype, w.n, w.k, w.sorted_index, gidx, gval, oidx, oval)
+    finally:
+        pkg.ds_topk_set_overrides(0, 0)
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3", "C5"])
+def test_sorted_and_unsorted_agree(pkg, oracle_mod, cfg):
+    w = make_workload(cfg, batch=4)
+    log("sorted/unsorted %s" % cfg)
+    a, av = gpu_topk(w.raw, w.dtype, w.n, w.k, True, True)
+    b, bv = gpu_topk(w.raw, w.dtype, w.n, w.k, False, True)
+    assert np.all(np.diff(a, axis=1) > 0)
+    assert np.array_equal(a, np.sort(b, axis=1))
+    order = np.argsort(b, axis=1)
+    assert np.array_equal(av, np.take_along_axis(bv, order, axis=1))
