@@ -157,9 +157,12 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
  * Tuning overrides, process-wide (for tests and measurements):
  * segments > 0 forces that many workgroups per row (clamped to what the row
  * length allows); 0 restores the automatic choice.  tile_seed changes the
- * pseudo-random tile visiting order (the result never depends on it).
+ * pseudo-random tile visiting order (the result never depends on it); 0
+ * restores the default.  flags: DS_TOPK_FORCE_BITONIC makes index-ordered
+ * output always use the bitonic sort instead of the bitmap ranking.
  */
-void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed);
+#define DS_TOPK_FORCE_BITONIC 1
+void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed, int32_t flags);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int ds_topk_version(void);

@@ -79,7 +79,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk_plan_for.restype = ci
     lib.ds_topk_plan_for.argtypes = [ci, i64, i64, i64, i32, ci, ci, ctypes.POINTER(ds_topk_plan)]
     lib.ds_topk_set_overrides.restype = None
-    lib.ds_topk_set_overrides.argtypes = [i32, ctypes.c_uint32]
+    lib.ds_topk_set_overrides.argtypes = [i32, ctypes.c_uint32, i32]
     lib.ds_topk_version.restype = ci
     lib.ds_topk_version.argtypes = []
     if path is None:
@@ -117,8 +117,11 @@ def ds_topk_plan_for(dtype: int, batch: int, n: int, row_stride: int, k: int, so
     return st, plan
 
 
-def ds_topk_set_overrides(segments: int = 0, tile_seed: int = 0) -> None:
-    load_library().ds_topk_set_overrides(segments, tile_seed)
+DS_TOPK_FORCE_BITONIC = 1
+
+
+def ds_topk_set_overrides(segments: int = 0, tile_seed: int = 0, flags: int = 0) -> None:
+    load_library().ds_topk_set_overrides(segments, tile_seed, flags)
 
 
 def ds_topk_version() -> int:

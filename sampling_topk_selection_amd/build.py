@@ -14,6 +14,8 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ds_topk.hip")
 DEPS = [SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(ROOT, "include", "ds_topk.h")]
 LIB = os.path.join(HERE, "libds_topk.so")
+CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
+CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,26 +32,34 @@ FLAGS = [
 ]
 
 
-def stale() -> bool:
-    if not os.path.exists(LIB):
+def stale(lib: str = LIB, deps=None) -> bool:
+    deps = DEPS if deps is None else deps
+    if not os.path.exists(lib):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(d) > t for d in DEPS)
+    t = os.path.getmtime(lib)
+    return any(os.path.getmtime(d) > t for d in deps)
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and not stale():
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _hipcc(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                             "-o", tmp, SRC]
+                             "-o", tmp, src]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Build libds_topk.so (the library) and libds_calib.so (benchmark
+    calibration kernels)."""
+    if force or stale():
+        _hipcc(SRC, LIB, verbose)
+    if force or stale(CALIB_LIB, [CALIB_SRC]):
+        _hipcc(CALIB_SRC, CALIB_LIB, verbose)
     return LIB
 
 

@@ -37,6 +37,7 @@ int fail(int status, const char* fmt, ...) {
 
 std::atomic<int32_t> g_force_segs{0};
 std::atomic<uint32_t> g_tile_seed{0x2545F491u};
+std::atomic<int32_t> g_flags{0};
 
 struct Plan {
     int eb = 0;    // element bytes
@@ -265,6 +266,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.ws_ticket = ws->ticket;
         prm.flag = flag;
         prm.flag_value = flag_value;
+        prm.flags = g_flags.load();
         e = launch(pl, prm, rows, stream);
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
     }
@@ -331,9 +333,10 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
     return DS_OK;
 }
 
-void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed) {
+void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed, int32_t flags) {
     g_force_segs.store(segments > 0 ? segments : 0);
     g_tile_seed.store(tile_seed ? tile_seed : 0x2545F491u);
+    g_flags.store(flags & DS_TOPK_FORCE_BITONIC);
 }
 
 int ds_topk_version(void) { return kVersion; }

@@ -107,159 +107,291 @@ struct PreFilter<Elem<4>> {
 };
 
 // ------------------------------------------------------------------ shared
+constexpr int kHistBits = 11;  // radix-select digit width
+constexpr int kBins = 1 << kHistBits;
+constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
+
 template <int CAP>
 struct Smem {
-    u64 buf[CAP];     // candidate composites
-    u32 hist[256];    // radix-select histogram
-    u64 L;            // admission bound: admit iff composite >= L
-    u64 kth;          // k-th composite after the last compaction
-    u64 tmin;
-    u32 count;        // entries in buf
-    u32 newcount;
-    u32 sel_digit, sel_r, sel_c;
+    u64 buf[CAP];      // candidate composites
+    u32 hist[kBins];   // radix-select histogram
+    u64 red[16][3];    // per-wave OR / AND / MIN
+    u64 L;             // admission bound: admit iff composite >= L
+    u64 kth;           // k-th composite after the last compaction
+    u32 count;         // entries in buf
+    u32 sel_digit, sel_r, sel_c, sel_above;
+    u32 wsum[16];      // per-wave partial sums
     u32 nan;
     u32 last;
     u32 seg_count[256];  // merge: entries per segment
 };
 
+// Optional instrumentation hook (phase timestamps); compiled out by default.
+#ifndef DSTK_PHASE
+#define DSTK_PHASE(i) ((void)0)
+#endif
+
 // ------------------------------------------------------------------ wave helpers
+// Cross-lane steps use DPP (row_shr, quad_perm, row mirrors, row_bcast15/31),
+// which stay in the VALU; __shfl_* would be an LDS round trip per step.
 __device__ __forceinline__ u32 lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ u32 mbcnt(u64 m) {
     return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
 }
 
-__device__ __forceinline__ u32 wave_incl_scan(u32 v) {
-    const u32 lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        u32 t = __shfl_up(v, o, kWave);
-        if (lane >= (u32)o) v += t;
-    }
-    return v;
+// Inclusive prefix sum across the 64 lanes (all lanes active).
+__device__ __forceinline__ u32 wave_incl_scan(u32 x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
 }
 
-__device__ __forceinline__ u64 wave_min_u64(u64 v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        u64 t = __shfl_xor(v, o, kWave);
-        v = t < v ? t : v;
+// Reductions across the 64 lanes; the result is wave-uniform.
+#define DSTK_WAVE_REDUCE(NAME, OPEXPR, IDENT)                                         \
+    __device__ __forceinline__ u32 NAME(u32 v) {                                      \
+        u32 t;                                                                        \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0xB1, 0xF, 0xF, false); v = OPEXPR;  \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0x4E, 0xF, 0xF, false); v = OPEXPR;  \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0x141, 0xF, 0xF, false); v = OPEXPR; \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0x140, 0xF, 0xF, false); v = OPEXPR; \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0x142, 0xA, 0xF, false); v = OPEXPR; \
+        t = __builtin_amdgcn_update_dpp(IDENT, v, 0x143, 0xC, 0xF, false); v = OPEXPR; \
+        return __builtin_amdgcn_readlane(v, 63);                                      \
     }
-    return v;
+DSTK_WAVE_REDUCE(wave_or, (v | t), 0u)
+DSTK_WAVE_REDUCE(wave_and, (v & t), 0xFFFFFFFFu)
+DSTK_WAVE_REDUCE(wave_min, (t < v ? t : v), 0xFFFFFFFFu)
+#undef DSTK_WAVE_REDUCE
+
+__device__ __forceinline__ u64 wave_or64(u64 v) { return ((u64)wave_or((u32)(v >> 32)) << 32) | wave_or((u32)v); }
+__device__ __forceinline__ u64 wave_and64(u64 v) {
+    return ((u64)wave_and((u32)(v >> 32)) << 32) | wave_and((u32)v);
+}
+__device__ __forceinline__ u64 wave_min64(u64 v) {
+    const u32 hi = wave_min((u32)(v >> 32));
+    const u32 lo = wave_min((u32)(v >> 32) == hi ? (u32)v : 0xFFFFFFFFu);
+    return ((u64)hi << 32) | lo;
 }
 
-// Append v (where pred) to buf, one LDS atomic per wave.
-__device__ __forceinline__ void wave_append(u64* buf, u32* counter, u64 v, bool pred) {
-    const u64 m = __ballot(pred);
-    if (m == 0) return;
+// Reserve `c` consecutive slots per lane behind *counter (one LDS atomic per
+// wave); returns this lane's first slot, or ~0u if the wave has nothing.
+__device__ __forceinline__ u32 wave_reserve(u32* counter, u32 c) {
+    const u32 incl = wave_incl_scan(c);
+    const u32 tot = __builtin_amdgcn_readlane(incl, 63);
+    if (tot == 0) return ~0u;
     u32 base = 0;
-    if (lane_id() == 0) base = atomicAdd(counter, (u32)__popcll(m));
+    if (lane_id() == 0) base = atomicAdd(counter, tot);
     base = __builtin_amdgcn_readfirstlane(base);
-    if (pred) buf[base + mbcnt(m)] = v;
+    return base + incl - c;
 }
 
-// ------------------------------------------------------------------ radix select
-// The r-th largest (r >= 1) of the distinct composites buf[0, cnt).  MSD
-// radix over 8-bit digits: first the value-key bits, then the column bits
-// that can differ (column < 2^idx_bits).  Stops as soon as the bin holding
-// the answer is needed whole; the answer is then that bin's minimum.
-template <class E, int WG, int CAP>
-__device__ u64 select_rth(Smem<CAP>& sm, u32 cnt, u32 r, int idx_bits) {
-    const u32 tid = threadIdx.x;
-    const int key_lo = 64 - E::kKeyBits;
-    u64 prefix = 0, mask = 0;
-    int hi = 64;
-    for (;;) {
-        int width, shift;
-        if (hi > key_lo) {
-            width = 8;
-            shift = hi - 8;
-        } else {
-            if (hi == key_lo) {
-                // ~column has all-one bits above idx_bits for every entry
-                const u64 ones = idx_bits >= 32 ? 0ull
-                                                : ((((u64)1 << (32 - idx_bits)) - 1) << (E::kIdxShift + idx_bits));
-                prefix |= ones;
-                mask |= ones;
-                hi = E::kIdxShift + idx_bits;
-            }
-            if (hi <= E::kIdxShift) break;  // unreachable for distinct entries
-            width = hi - E::kIdxShift < 8 ? hi - E::kIdxShift : 8;
-            shift = hi - width;
-        }
-        for (u32 i = tid; i < 256; i += WG) sm.hist[i] = 0;
-        __syncthreads();
-        const u32 wmask = (1u << width) - 1u;
-        for (u32 i = tid; i < cnt; i += WG) {
-            const u64 e = sm.buf[i];
-            if ((e & mask) == prefix) atomicAdd(&sm.hist[(u32)(e >> shift) & wmask], 1u);
-        }
-        __syncthreads();
-        if (tid < kWave) {
-            // lane l owns bins 255-4l .. 252-4l (descending)
-            const u32 l = tid;
-            const u32 h0 = sm.hist[255 - 4 * l], h1 = sm.hist[254 - 4 * l];
-            const u32 h2 = sm.hist[253 - 4 * l], h3 = sm.hist[252 - 4 * l];
-            const u32 s = h0 + h1 + h2 + h3;
-            const u32 incl = wave_incl_scan(s);
-            const u32 excl = incl - s;
-            if (excl < r && r <= incl) {
-                u32 rr = r - excl, d, c;
-                if (rr <= h0) {
-                    d = 255 - 4 * l; c = h0;
-                } else if (rr <= h0 + h1) {
-                    rr -= h0; d = 254 - 4 * l; c = h1;
-                } else if (rr <= h0 + h1 + h2) {
-                    rr -= h0 + h1; d = 253 - 4 * l; c = h2;
-                } else {
-                    rr -= h0 + h1 + h2; d = 252 - 4 * l; c = h3;
-                }
-                sm.sel_digit = d;
-                sm.sel_r = rr;
-                sm.sel_c = c;
-            }
-            if (l == 0) sm.tmin = ~0ull;
-        }
-        __syncthreads();
-        const u32 d = sm.sel_digit, c = sm.sel_c;
-        r = sm.sel_r;
-        prefix |= (u64)d << shift;
-        mask |= (u64)wmask << shift;
-        if (c == r) break;
-        hi = shift;
-    }
-    // The answer is the least entry matching prefix under mask.
-    u64 lm = ~0ull;
-    for (u32 i = tid; i < cnt; i += WG) {
-        const u64 e = sm.buf[i];
-        if ((e & mask) == prefix && e < lm) lm = e;
-    }
-    lm = wave_min_u64(lm);
-    if (lane_id() == 0 && lm != ~0ull) atomicMin((unsigned long long*)&sm.tmin, (unsigned long long)lm);
+// ------------------------------------------------------------------ block helpers
+// Exclusive prefix sum of one value per thread, in thread order; *total gets
+// the block sum.  Separate consecutive calls by a barrier.
+template <int WG, int CAP>
+__device__ u32 block_excl_scan(Smem<CAP>& sm, u32 v, u32* total) {
+    const u32 wave = threadIdx.x / kWave;
+    const u32 incl = wave_incl_scan(v);
+    if (lane_id() == kWave - 1) sm.wsum[wave] = incl;
     __syncthreads();
-    return sm.tmin;
+    u32 off = 0, tot = 0;
+#pragma unroll
+    for (u32 w = 0; w < WG / kWave; ++w) {
+        const u32 s = sm.wsum[w];
+        off += w < wave ? s : 0u;
+        tot += s;
+    }
+    *total = tot;
+    return off + incl - v;
 }
 
-// Reduce buf[0, cnt) to its k largest entries (cnt > k); sets L and kth.
-template <class E, int WG, int CAP>
-__device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k, int idx_bits) {
+// OR, AND and MIN over the entries of buf[lo, hi) whose bits under `mask`
+// equal `prefix`.  Separate consecutive calls by a barrier.
+template <int WG, int CAP>
+__device__ void block_reduce(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, u64& o, u64& a, u64& mn) {
     const u32 tid = threadIdx.x;
-    const u64 T = select_rth<E, WG, CAP>(sm, cnt, k, idx_bits);
+    u64 vo = 0, va = ~0ull, vm = ~0ull;
+    for (u32 i = lo + tid; i < hi; i += WG) {
+        const u64 e = sm.buf[i];
+        if ((e & mask) == prefix) {
+            vo |= e;
+            va &= e;
+            vm = e < vm ? e : vm;
+        }
+    }
+    vo = wave_or64(vo);
+    va = wave_and64(va);
+    vm = wave_min64(vm);
+    const u32 wave = tid / kWave;
+    if (lane_id() == 0) {
+        sm.red[wave][0] = vo;
+        sm.red[wave][1] = va;
+        sm.red[wave][2] = vm;
+    }
+    __syncthreads();
+    o = 0;
+    a = ~0ull;
+    mn = ~0ull;
+#pragma unroll
+    for (u32 w = 0; w < WG / kWave; ++w) {
+        o |= sm.red[w][0];
+        a &= sm.red[w][1];
+        mn = sm.red[w][2] < mn ? sm.red[w][2] : mn;
+    }
+}
+
+// Histogram of the digit (e >> shift) & (kBins-1) over the entries of
+// buf[lo, hi) matching (prefix, mask); then the bin holding the r-th largest
+// (r >= 1).  Leaves sel_digit, sel_r (rank inside the bin), sel_c (bin size)
+// and sel_above (entries in higher bins) in shared memory.
+template <int WG, int CAP>
+__device__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, int shift, u32 r) {
+    const u32 tid = threadIdx.x;
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    if (tid == 0) {  // overwritten below unless r exceeds the matching count
+        sm.sel_digit = 0;
+        sm.sel_r = 0;
+        sm.sel_c = 0;
+        sm.sel_above = 0;
+    }
+    __syncthreads();
+    for (u32 i = lo + tid; i < hi; i += WG) {
+        const u64 e = sm.buf[i];
+        if ((e & mask) == prefix) atomicAdd(&sm.hist[(u32)(e >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    constexpr int kPer = kBins / WG;  // bins per thread, highest bins first
+    u32 h[kPer];
+    u32 s = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        h[j] = sm.hist[kBins - 1 - tid * kPer - j];
+        s += h[j];
+    }
+    u32 tot;
+    const u32 excl = block_excl_scan<WG, CAP>(sm, s, &tot);
+    if (excl < r && r <= excl + s) {
+        u32 acc = excl;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (acc < r && r <= acc + h[j]) {
+                sm.sel_digit = kBins - 1 - tid * kPer - j;
+                sm.sel_r = r - acc;
+                sm.sel_c = h[j];
+                sm.sel_above = acc;
+            }
+            acc += h[j];
+        }
+    }
+    __syncthreads();
+}
+
+// Window of kHistBits bits whose top bit is the highest bit set in diff.
+__device__ __forceinline__ int window_shift(u64 diff) {
+    const int msb = 63 - __clzll((long long)diff);
+    return msb >= kHistBits - 1 ? msb - (kHistBits - 1) : 0;
+}
+__device__ __forceinline__ u64 bits_above(int shift) {
+    return shift + kHistBits >= 64 ? 0ull : (~0ull << (shift + kHistBits));
+}
+
+// ------------------------------------------------------------------ compaction
+// Reduce buf[0, cnt) (distinct composites, cnt > k) to its k largest, in
+// buf[0, k); sets kth (the least kept) and L = kth + 1.
+//
+// Radix select with 11-bit digits.  Each level's window starts at the
+// highest bit where the still-undecided entries differ, so concentrated
+// value distributions still spread over the bins.  After the first level
+// the buffer is partitioned once: entries in higher bins are kept outright,
+// the boundary bin is moved next to them, and later levels only look at that
+// boundary list.  Placement uses block prefix sums, not atomics, so the
+// result order is a deterministic function of the buffer order.
+template <class E, int WG, int CAP>
+__device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k) {
+    const u32 tid = threadIdx.x;
     constexpr int kItems = CAP / WG;
+    u64 o, a, mn;
+    block_reduce<WG, CAP>(sm, 0, cnt, 0ull, 0ull, o, a, mn);
+    int shift = window_shift(o ^ a);
+    u64 mask = bits_above(shift);
+    u64 prefix = a & mask;
+    block_hist_find<WG, CAP>(sm, 0, cnt, prefix, mask, shift, k);
+    const u32 b = sm.sel_digit, above = sm.sel_above, c = sm.sel_c;
+    u32 r = sm.sel_r;
+
+    // Partition: higher bins to [0, above), bin b to [above, above + c).
     u64 mine[kItems];
+    u32 nd = 0, nm = 0;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const u32 i = tid + j * WG;
         mine[j] = i < cnt ? sm.buf[i] : 0ull;
+        const u32 d = (u32)(mine[j] >> shift) & (kBins - 1);
+        nd += (i < cnt && d > b) ? 1u : 0u;
+        nm += (i < cnt && d == b) ? 1u : 0u;
     }
-    if (tid == 0) sm.newcount = 0;
-    __syncthreads();
+    u32 tot;
+    const u32 ex = block_excl_scan<WG, CAP>(sm, nd | (nm << 16), &tot);  // counts < 2^16
+    u32 pd = ex & 0xFFFFu, pm = above + (ex >> 16);
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
         const u32 i = tid + j * WG;
-        wave_append(sm.buf, &sm.newcount, mine[j], i < cnt && mine[j] >= T);
+        const u32 d = (u32)(mine[j] >> shift) & (kBins - 1);
+        if (i < cnt && d > b) sm.buf[pd++] = mine[j];
+        if (i < cnt && d == b) sm.buf[pm++] = mine[j];
     }
     __syncthreads();
+    prefix |= (u64)b << shift;
+    mask |= (u64)(kBins - 1) << shift;
+
+    const u32 lo = above, hi = above + c;
+    u64 T;
+    if (r == c) {
+        block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
+        T = mn;
+    } else {
+        // Each level fixes at least one more bit, so 64 / kHistBits + 1
+        // levels always suffice; the bound only guards the loop.
+        T = 0;
+        for (int level = 0; level < 64 / kHistBits + 2; ++level) {
+            block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
+            shift = window_shift(o ^ a);
+            // Keep the bits fixed so far: a window clamped at bit 0 can
+            // overlap them.
+            mask |= bits_above(shift);
+            prefix = a & mask;
+            block_hist_find<WG, CAP>(sm, lo, hi, prefix, mask, shift, r);
+            const u32 d2 = sm.sel_digit, c2 = sm.sel_c, r2 = sm.sel_r;
+            prefix |= (u64)d2 << shift;
+            mask |= (u64)(kBins - 1) << shift;
+            if (r2 == c2) {
+                block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
+                T = mn;
+                break;
+            }
+            r = r2;
+        }
+        // keep the boundary entries >= T, packed right after the definite ones
+        u32 nk = 0;
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const u32 i = lo + tid + j * WG;
+            mine[j] = i < hi ? sm.buf[i] : 0ull;
+            nk += (i < hi && mine[j] >= T) ? 1u : 0u;
+        }
+        __syncthreads();  // wsum reuse
+        u32 pk = lo + block_excl_scan<WG, CAP>(sm, nk, &tot);
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const u32 i = lo + tid + j * WG;
+            if (i < hi && mine[j] >= T) sm.buf[pk++] = mine[j];
+        }
+    }
     if (tid == 0) {
         sm.count = k;
         sm.kth = T;
@@ -269,8 +401,12 @@ __device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k, int idx_bits) {
 }
 
 // ------------------------------------------------------------------ output
+// Writes the k entries of buf[0, k).  Index order, when asked for, comes
+// from a bitmap of the selected columns and a prefix popcount over it (when
+// the row's bitmap fits in the free LDS), else from a bitonic sort.
 template <class E, int WG, int CAP>
-__device__ void emit(Smem<CAP>& sm, u32 k, int sorted, int retval, int32_t* out_idx, void* out_val) {
+__device__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
+                     void* out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
     VT* ov = (VT*)out_val;
@@ -279,6 +415,39 @@ __device__ void emit(Smem<CAP>& sm, u32 k, int sorted, int retval, int32_t* out_
             const u64 e = sm.buf[i];
             out_idx[i] = (int32_t)comp_col<E>(e);
             if (retval) ov[i] = (VT)E::bits(comp_key<E>(e));
+        }
+        return;
+    }
+    const u32 words = (n + 31) / 32;
+    if (!(flags & kFlagBitonic) && (u64)k * 8 + (u64)words * 8 <= (u64)CAP * 8) {
+        u32* bm = (u32*)(sm.buf + k);
+        u32* pre = bm + words;
+        for (u32 w = tid; w < words; w += WG) bm[w] = 0;
+        __syncthreads();
+        for (u32 i = tid; i < k; i += WG) {
+            const u32 c = comp_col<E>(sm.buf[i]);
+            atomicOr(&bm[c >> 5], 1u << (c & 31));
+        }
+        __syncthreads();
+        const u32 per = (words + WG - 1) / WG;
+        const u32 w0 = tid * per;
+        u32 s = 0;
+        for (u32 j = 0; j < per; ++j)
+            if (w0 + j < words) s += __popc(bm[w0 + j]);
+        u32 tot;
+        u32 run = block_excl_scan<WG, CAP>(sm, s, &tot);
+        for (u32 j = 0; j < per; ++j)
+            if (w0 + j < words) {
+                pre[w0 + j] = run;
+                run += __popc(bm[w0 + j]);
+            }
+        __syncthreads();
+        for (u32 i = tid; i < k; i += WG) {
+            const u64 e = sm.buf[i];
+            const u32 c = comp_col<E>(e);
+            const u32 pos = pre[c >> 5] + __popc(bm[c >> 5] & ((1u << (c & 31)) - 1u));
+            out_idx[pos] = (int32_t)c;
+            if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
         }
         return;
     }
@@ -295,10 +464,10 @@ __device__ void emit(Smem<CAP>& sm, u32 k, int sorted, int retval, int32_t* out_
                 const u32 i = 2 * t - (t & (stride - 1));
                 const u32 j = i + stride;
                 const bool up = (i & size) == 0;
-                const u64 a = sm.buf[i], b = sm.buf[j];
-                if ((a > b) == up) {
-                    sm.buf[i] = b;
-                    sm.buf[j] = a;
+                const u64 x = sm.buf[i], y = sm.buf[j];
+                if ((x > y) == up) {
+                    sm.buf[i] = y;
+                    sm.buf[j] = x;
                 }
             }
             __syncthreads();
@@ -332,6 +501,7 @@ struct Params {
     u32* ws_ticket;    // [batch], zero between calls
     int32_t* flag;     // set to flag_value when a NaN is seen
     int32_t flag_value;
+    int32_t flags;     // kFlag* bits
 };
 
 __device__ __forceinline__ u32 hash32(u32 x) {
@@ -386,6 +556,7 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         sm.kth = 0;
         sm.nan = 0;
     }
+    DSTK_PHASE(0);
     __syncthreads();
 
     PreFilter<E> pf;
@@ -414,50 +585,45 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         }
         if (__ballot(any != 0) != 0) {
             // Exact test on every element slot; one LDS reservation per wave.
-            constexpr int kSlots = VPT * 4 * (EB == 2 ? 2 : 1);
-            u64 masks[kSlots];
-            u32 total = 0;
+            constexpr int kSlots = VPT * E::kPerVec;
+            constexpr int kPerDword = EB == 2 ? 2 : 1;
+            u32 pm = 0, c = 0;
 #pragma unroll
             for (int s = 0; s < kSlots; ++s) {
-                const int j = s / (kSlots / VPT);
-                const int w = (s % (kSlots / VPT)) / (EB == 2 ? 2 : 1);
-                const int hh = EB == 2 ? (s & 1) : 0;
+                const int j = s / E::kPerVec;
+                const int w = (s % E::kPerVec) / kPerDword;
+                const int hh = s % kPerDword;
                 const u32 d = w == 0 ? cur[j].x : w == 1 ? cur[j].y : w == 2 ? cur[j].z : cur[j].w;
                 const u32 bits = EB == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
                 const int vi = vb + j * WG + (int)tid;
-                const u32 col = (u32)vi * E::kPerVec + (u32)(w * (EB == 2 ? 2 : 1) + hh);
+                const u32 col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
                 const bool valid = vi < v1 && col < (u32)p.n;
                 saw_nan |= valid && E::is_nan(bits);
-                const u64 c = compose<E>(E::key(bits), col);
-                masks[s] = __ballot(valid && c >= L);
-                total += (u32)__popcll(masks[s]);
+                const bool ok = valid && compose<E>(E::key(bits), col) >= L;
+                pm |= (u32)ok << s;
+                c += ok;
             }
-            if (total) {
-                u32 base = 0;
-                if (lane_id() == 0) base = atomicAdd(&sm.count, total);
-                base = __builtin_amdgcn_readfirstlane(base);
+            u32 pos = wave_reserve(&sm.count, c);
+            if (pos != ~0u) {
 #pragma unroll
                 for (int s = 0; s < kSlots; ++s) {
-                    const u64 m = masks[s];
-                    if (m == 0) continue;
-                    if ((m >> lane_id()) & 1ull) {
-                        const int j = s / (kSlots / VPT);
-                        const int w = (s % (kSlots / VPT)) / (EB == 2 ? 2 : 1);
-                        const int hh = EB == 2 ? (s & 1) : 0;
+                    if ((pm >> s) & 1u) {
+                        const int j = s / E::kPerVec;
+                        const int w = (s % E::kPerVec) / kPerDword;
+                        const int hh = s % kPerDword;
                         const u32 d = w == 0 ? cur[j].x : w == 1 ? cur[j].y : w == 2 ? cur[j].z : cur[j].w;
                         const u32 bits = EB == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
                         const int vi = vb + j * WG + (int)tid;
-                        const u32 col = (u32)vi * E::kPerVec + (u32)(w * (EB == 2 ? 2 : 1) + hh);
-                        sm.buf[base + mbcnt(m)] = compose<E>(E::key(bits), col);
+                        const u32 col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
+                        sm.buf[pos++] = compose<E>(E::key(bits), col);
                     }
-                    base += (u32)__popcll(m);
                 }
             }
         }
         __syncthreads();
         const u32 cnt = sm.count;
         if (cnt > (u32)(CAP - kTileElems)) {
-            compact_to_k<E, WG, CAP>(sm, cnt, k, p.idx_bits);
+            compact_to_k<E, WG, CAP>(sm, cnt, k);
             L = sm.L;
             pf.set(L);
         }
@@ -465,31 +631,29 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         for (int j = 0; j < VPT; ++j) cur[j] = nxt[j];
     }
 
+    DSTK_PHASE(1);
     // Final reduction of this segment to at most k entries.
     u32 cnt = sm.count;
     if (cnt > k) {
-        compact_to_k<E, WG, CAP>(sm, cnt, k, p.idx_bits);
+        compact_to_k<E, WG, CAP>(sm, cnt, k);
         cnt = k;
     } else if (cnt == k && p.segs > 1) {
         // k-th = least entry; a valid lower bound for the whole row
-        if (tid == 0) sm.tmin = ~0ull;
-        __syncthreads();
-        u64 lm = ~0ull;
-        for (u32 i = tid; i < cnt; i += WG) lm = sm.buf[i] < lm ? sm.buf[i] : lm;
-        lm = wave_min_u64(lm);
-        if (lane_id() == 0) atomicMin((unsigned long long*)&sm.tmin, (unsigned long long)lm);
-        __syncthreads();
-        if (tid == 0) sm.kth = sm.tmin;
+        u64 o, a, mn;
+        block_reduce<WG, CAP>(sm, 0, cnt, 0ull, 0ull, o, a, mn);
+        if (tid == 0) sm.kth = mn;
         __syncthreads();
     }
+    DSTK_PHASE(2);
 
     if (saw_nan) sm.nan = 1;  // benign race: every writer stores 1
 
     if (p.segs == 1) {
-        emit<E, WG, CAP>(sm, k, p.sorted, p.retval, p.out_idx + (int64_t)row * k,
+        emit<E, WG, CAP>(sm, k, (u32)p.n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
                          p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
         __syncthreads();
         if (tid == 0 && sm.nan) *p.flag = p.flag_value;
+        DSTK_PHASE(6);
         return;
     }
 
@@ -501,18 +665,22 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         p.ws_count[slot] = cnt;
         p.ws_kth[slot] = cnt == k ? sm.kth : 0ull;
     }
-    __threadfence();
     __syncthreads();
     if (tid == 0) {
+        // release this workgroup's stores (ordered before by the barrier) to
+        // the device, then take a ticket; the last ticket merges
+        __threadfence();
         const u32 prev = atomicAdd(&p.ws_ticket[row], 1u);
         sm.last = prev == (u32)p.segs - 1;
+        if (sm.last) __threadfence();
     }
     __syncthreads();
     if (!sm.last) {
         if (tid == 0 && sm.nan) *p.flag = p.flag_value;
+        DSTK_PHASE(3);
         return;
     }
-    __threadfence();
+    DSTK_PHASE(4);
 
     // Merge: every element of the row's top-k is in some segment's list, and
     // no segment's k-th composite exceeds the row's k-th, so the largest of
@@ -542,31 +710,41 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
     constexpr int kMI = kTileElems / WG;  // merge entries per thread per step
     const u32 total = S * k;
     for (u32 base = 0; base < total; base += WG * kMI) {
+        u64 e[kMI];
+        u32 pm = 0, c = 0;
 #pragma unroll
         for (int j = 0; j < kMI; ++j) {
             const u32 f = base + j * WG + tid;
-            bool ok = f < total;
-            u64 e = 0;
-            if (ok) {
+            e[j] = 0;
+            if (f < total) {
                 const u32 s = f / k, jj = f - s * k;
-                ok = jj < sm.seg_count[s];
-                if (ok) e = rc[f];
+                if (jj < sm.seg_count[s]) e[j] = rc[f];
             }
-            wave_append(sm.buf, &sm.count, e, ok && e >= L);
+            const bool ok = e[j] != 0 && e[j] >= L;  // composites of real elements are nonzero
+            pm |= (u32)ok << j;
+            c += ok;
+        }
+        u32 pos = wave_reserve(&sm.count, c);
+        if (pos != ~0u) {
+#pragma unroll
+            for (int j = 0; j < kMI; ++j)
+                if ((pm >> j) & 1u) sm.buf[pos++] = e[j];
         }
         __syncthreads();
         const u32 c2 = sm.count;
         if (c2 > (u32)(CAP - kTileElems)) {
-            compact_to_k<E, WG, CAP>(sm, c2, k, p.idx_bits);
+            compact_to_k<E, WG, CAP>(sm, c2, k);
             L = sm.L;
         }
     }
     cnt = sm.count;
-    if (cnt > k) compact_to_k<E, WG, CAP>(sm, cnt, k, p.idx_bits);
-    emit<E, WG, CAP>(sm, k, p.sorted, p.retval, p.out_idx + (int64_t)row * k,
+    if (cnt > k) compact_to_k<E, WG, CAP>(sm, cnt, k);
+    DSTK_PHASE(5);
+    emit<E, WG, CAP>(sm, k, (u32)p.n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
                      p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
     __syncthreads();
     if (tid == 0 && sm.nan) *p.flag = p.flag_value;
+    DSTK_PHASE(6);
 }
 
 }  // namespace dstk
