@@ -142,7 +142,8 @@ const char* ds_topk_last_error(void);
 typedef struct ds_topk_plan {
     int32_t segments;        /* workgroups per row; > 1 means split rows + merge */
     int32_t threads;         /* threads per workgroup */
-    int32_t vectors_per_tile_thread; /* 16-byte loads per thread per tile */
+    int32_t tiles_per_chunk; /* tiles whose loads are in flight together; a tile is
+                                one 16-byte vector per thread */
     int32_t capacity;        /* candidate-buffer entries per workgroup (LDS) */
     int32_t segment_vectors; /* 16-byte vectors per segment (last may be shorter) */
     int32_t tiles_per_segment;

@@ -49,7 +49,7 @@ class TopkError(RuntimeError):
 
 class ds_topk_plan(ctypes.Structure):
     _fields_ = [("segments", ctypes.c_int32), ("threads", ctypes.c_int32),
-                ("vectors_per_tile_thread", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("tiles_per_chunk", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("segment_vectors", ctypes.c_int32), ("tiles_per_segment", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 

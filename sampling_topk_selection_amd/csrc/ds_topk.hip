@@ -21,6 +21,7 @@ constexpr int kVersion = 100;       // 0.1.0
 constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS count each)
 constexpr int kTargetWG = 512;      // about two workgroups per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
+constexpr int kLoadsPerThread = 4;  // tiles per chunk: 16-byte loads each thread has in flight
 constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
 
 thread_local std::string g_err;
@@ -40,15 +41,16 @@ std::atomic<uint32_t> g_tile_seed{0x2545F491u};
 std::atomic<int32_t> g_flags{0};
 
 struct Plan {
-    int eb = 0;    // element bytes
-    int wg = 512;  // threads per workgroup
-    int vpt = 1;   // 16-byte loads per thread per tile
-    int cap = 0;   // LDS candidate capacity
+    int eb = 0;     // element bytes
+    int wg = 512;   // threads per workgroup
+    int vpt = 1;    // tiles per chunk (16-byte loads in flight per thread)
+    int depth = 2;  // tiles in flight beyond the one being filtered
+    int cap = 0;    // LDS candidate capacity
+    int pub_cap = 0;  // candidates a segment may publish
     int segs = 1;
     int seg_vecs = 0;
     int n_vec = 0;
     int tiles = 0;
-    int idx_bits = 0;
     int64_t rows_per_launch = 0;
     int64_t ws_bytes = 0;
 };
@@ -74,14 +76,10 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     pl->eb = dtype == DS_DTYPE_BF16 ? 2 : 4;
     const int epv = 16 / pl->eb;
     pl->wg = 512;
-    if (pl->eb == 2) {
-        pl->vpt = k <= 1024 ? 1 : 2;
-        pl->cap = k <= 1024 ? 8192 : 16384;
-    } else {
-        pl->vpt = 2;
-        pl->cap = k <= 1024 ? 8192 : 16384;
-    }
-    const int tile_vecs = pl->wg * pl->vpt;
+    pl->vpt = kLoadsPerThread;  // 16-byte loads in flight per thread (one chunk)
+    pl->depth = 0;
+    pl->cap = k <= 1024 ? 8192 : 16384;
+    pl->pub_cap = 2 * k + 1024 < pl->cap ? 2 * k + 1024 : pl->cap;
     pl->n_vec = (int)((n + epv - 1) / epv);
     int64_t s;
     const int32_t forced = g_force_segs.load();
@@ -95,19 +93,20 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     if (s > kMaxSegs) s = kMaxSegs;
     if (s > pl->n_vec) s = pl->n_vec;
     if (s < 1) s = 1;
+    const int64_t by_rsrc = (pl->n_vec + dstk::kMaxSegVecs - 1) / dstk::kMaxSegVecs;
+    if (s < by_rsrc) s = by_rsrc;  // each segment fits one buffer resource
     pl->seg_vecs = (int)((pl->n_vec + s - 1) / s);
     pl->segs = (pl->n_vec + pl->seg_vecs - 1) / pl->seg_vecs;
-    pl->tiles = (pl->seg_vecs + tile_vecs - 1) / tile_vecs;
-    pl->idx_bits = n <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(n - 1));
+    pl->tiles = (pl->seg_vecs + pl->wg - 1) / pl->wg;
     const int64_t max_rows = kMaxGridWG / pl->segs;
     pl->rows_per_launch = batch < max_rows ? batch : max_rows;
     const int64_t r = pl->rows_per_launch;
     pl->ws_bytes = 256 + 256;  // NaN word
     if (pl->segs > 1) {
         pl->ws_bytes += ((r * 4 + 255) / 256) * 256;                          // tickets
-        pl->ws_bytes += ((r * pl->segs * 4 + 255) / 256) * 256;               // counts
-        pl->ws_bytes += ((r * pl->segs * 8 + 255) / 256) * 256;               // k-th keys
-        pl->ws_bytes += ((r * pl->segs * (int64_t)k * 8 + 255) / 256) * 256;  // candidates
+        pl->ws_bytes += ((r * pl->segs * 32 + 255) / 256) * 256;              // segment metadata
+        pl->ws_bytes += ((r * pl->segs * 4 * dstk::kBins + 255) / 256) * 256;  // digit directories
+        pl->ws_bytes += ((r * pl->segs * (int64_t)pl->pub_cap * 8 + 255) / 256) * 256;  // candidates
     }
     return DS_OK;
 }
@@ -120,8 +119,8 @@ struct Workspace {
     int64_t rows = 0, slots = 0, cands = 0;
     int32_t* nan_word = nullptr;
     uint32_t* ticket = nullptr;
-    uint32_t* count = nullptr;
-    uint64_t* kth = nullptr;
+    uint64_t* meta = nullptr;
+    uint32_t* dir = nullptr;
     uint64_t* cand = nullptr;
     int32_t* host_word = nullptr;  // pinned
     int32_t epoch = 0;
@@ -134,11 +133,11 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Make sure ws can hold `rows` rows of `segs` segments of k entries.
-int ensure(Workspace* ws, int64_t rows, int segs, int32_t k) {
+// Make sure ws can hold `rows` rows of `segs` segments of `per` entries.
+int ensure(Workspace* ws, int64_t rows, int segs, int32_t per) {
     const int64_t need_rows = segs > 1 ? rows : 0;
     const int64_t need_slots = segs > 1 ? rows * segs : 0;
-    const int64_t need_cands = segs > 1 ? rows * segs * (int64_t)k : 0;
+    const int64_t need_cands = segs > 1 ? rows * segs * (int64_t)per : 0;
     if (ws->base && need_rows <= ws->rows && need_slots <= ws->slots && need_cands <= ws->cands) return DS_OK;
     hipError_t e;
     if (!ws->host_word) {
@@ -149,7 +148,7 @@ int ensure(Workspace* ws, int64_t rows, int segs, int32_t k) {
     const int64_t slots2 = need_slots > ws->slots ? need_slots : ws->slots;
     const int64_t cands2 = need_cands > ws->cands ? need_cands : ws->cands;
     auto al = [](int64_t b) { return ((b + 255) / 256) * 256; };
-    const int64_t bytes = 256 + al(rows2 * 4) + al(slots2 * 4) + al(slots2 * 8) + al(cands2 * 8);
+    const int64_t bytes = 256 + al(rows2 * 4) + al(slots2 * 32) + al(slots2 * 4 * dstk::kBins) + al(cands2 * 8);
     if (ws->base) {
         // Earlier calls may still be queued on this stream: let them finish.
         e = hipDeviceSynchronize();
@@ -172,10 +171,10 @@ int ensure(Workspace* ws, int64_t rows, int segs, int32_t k) {
     p += 256;
     ws->ticket = (uint32_t*)p;
     p += al(rows2 * 4);
-    ws->count = (uint32_t*)p;
-    p += al(slots2 * 4);
-    ws->kth = (uint64_t*)p;
-    p += al(slots2 * 8);
+    ws->meta = (uint64_t*)p;
+    p += al(slots2 * 32);
+    ws->dir = (uint32_t*)p;
+    p += al(slots2 * 4 * dstk::kBins);
     ws->cand = (uint64_t*)p;
     ws->rows = rows2;
     ws->slots = slots2;
@@ -194,20 +193,21 @@ Workspace* workspace_for(int dev, hipStream_t s) {
     return slot.get();
 }
 
-template <int EB, int WG, int VPT, int CAP>
+template <int EB, int WG, int NV, int CAP>
 hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((dstk::topk_rows<EB, WG, VPT, CAP>), dim3((uint32_t)grid), dim3(WG), 0, s, prm);
+    hipLaunchKernelGGL((dstk::topk_rows<EB, WG, NV, CAP>), dim3((uint32_t)grid), dim3(WG), 0, s, prm);
     return hipGetLastError();
 }
 
+// The instances make_plan can choose (element bytes, capacity).
 hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s) {
     const int64_t grid = rows * pl.segs;
     if (pl.eb == 2) {
-        if (pl.cap == 8192) return launch_one<2, 512, 1, 8192>(prm, grid, s);
-        return launch_one<2, 512, 2, 16384>(prm, grid, s);
+        if (pl.cap == 8192) return launch_one<2, 512, kLoadsPerThread, 8192>(prm, grid, s);
+        return launch_one<2, 512, kLoadsPerThread, 16384>(prm, grid, s);
     }
-    if (pl.cap == 8192) return launch_one<4, 512, 2, 8192>(prm, grid, s);
-    return launch_one<4, 512, 2, 16384>(prm, grid, s);
+    if (pl.cap == 8192) return launch_one<4, 512, kLoadsPerThread, 8192>(prm, grid, s);
+    return launch_one<4, 512, kLoadsPerThread, 16384>(prm, grid, s);
 }
 
 int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
@@ -228,7 +228,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     Workspace* ws = workspace_for(dev, stream);
     std::lock_guard<std::mutex> g(ws->mu);
-    st = ensure(ws, pl.rows_per_launch, pl.segs, k);
+    st = ensure(ws, pl.rows_per_launch, pl.segs, pl.pub_cap);
     if (st) return st;
 
     int32_t* flag = status_dev;
@@ -254,15 +254,15 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.segs = pl.segs;
         prm.seg_vecs = pl.seg_vecs;
         prm.n_vec = pl.n_vec;
-        prm.idx_bits = pl.idx_bits;
         prm.seed = g_tile_seed.load();
         prm.sorted = sorted_index ? 1 : 0;
         prm.retval = return_value ? 1 : 0;
         prm.out_idx = out_idx + r0 * k;
         prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
         prm.ws_cand = ws->cand;
-        prm.ws_kth = ws->kth;
-        prm.ws_count = ws->count;
+        prm.ws_meta = ws->meta;
+        prm.ws_dir = ws->dir;
+        prm.pub_cap = pl.pub_cap;
         prm.ws_ticket = ws->ticket;
         prm.flag = flag;
         prm.flag_value = flag_value;
@@ -324,7 +324,7 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
     make_plan(dtype, batch, n, k, &pl);
     plan->segments = pl.segs;
     plan->threads = pl.wg;
-    plan->vectors_per_tile_thread = pl.vpt;
+    plan->tiles_per_chunk = pl.vpt;
     plan->capacity = pl.cap;
     plan->segment_vectors = pl.seg_vecs;
     plan->tiles_per_segment = pl.tiles;

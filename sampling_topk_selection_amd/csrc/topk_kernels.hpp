@@ -36,6 +36,11 @@ using u32 = uint32_t;
 using u64 = uint64_t;
 
 constexpr int kWave = 64;
+// Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle,
+// no index stride): byte-addressed loads with a range check.
+constexpr int kBufferWord3 = 0x00020000;
+// A segment is addressed by one buffer resource: at most 2^27 vectors (2 GiB).
+constexpr int kMaxSegVecs = 1 << 27;
 
 // ------------------------------------------------------------------ elements
 // Order-preserving keys: positive values get the sign bit set, negative
@@ -119,11 +124,13 @@ struct Smem {
     u64 L;             // admission bound: admit iff composite >= L
     u64 kth;           // k-th composite after the last compaction
     u32 count;         // entries in buf
-    u32 sel_digit, sel_r, sel_c, sel_above;
+    u32 sel_digit, sel_r, sel_c, sel_above, sel_total;
+    u32 d_hi;
     u32 wsum[16];      // per-wave partial sums
     u32 nan;
     u32 last;
-    u32 seg_count[256];  // merge: entries per segment
+    u32 newtotal;
+    u32 seg_count[256];  // merge: offset of each segment's list
 };
 
 // Optional instrumentation hook (phase timestamps); compiled out by default.
@@ -163,18 +170,18 @@ __device__ __forceinline__ u32 wave_incl_scan(u32 x) {
         t = __builtin_amdgcn_update_dpp(IDENT, v, 0x143, 0xC, 0xF, false); v = OPEXPR; \
         return __builtin_amdgcn_readlane(v, 63);                                      \
     }
-DSTK_WAVE_REDUCE(wave_or, (v | t), 0u)
-DSTK_WAVE_REDUCE(wave_and, (v & t), 0xFFFFFFFFu)
 DSTK_WAVE_REDUCE(wave_min, (t < v ? t : v), 0xFFFFFFFFu)
+DSTK_WAVE_REDUCE(wave_max, (t > v ? t : v), 0u)
 #undef DSTK_WAVE_REDUCE
 
-__device__ __forceinline__ u64 wave_or64(u64 v) { return ((u64)wave_or((u32)(v >> 32)) << 32) | wave_or((u32)v); }
-__device__ __forceinline__ u64 wave_and64(u64 v) {
-    return ((u64)wave_and((u32)(v >> 32)) << 32) | wave_and((u32)v);
-}
 __device__ __forceinline__ u64 wave_min64(u64 v) {
     const u32 hi = wave_min((u32)(v >> 32));
     const u32 lo = wave_min((u32)(v >> 32) == hi ? (u32)v : 0xFFFFFFFFu);
+    return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 wave_max64(u64 v) {
+    const u32 hi = wave_max((u32)(v >> 32));
+    const u32 lo = wave_max((u32)(v >> 32) == hi ? (u32)v : 0u);
     return ((u64)hi << 32) | lo;
 }
 
@@ -190,11 +197,38 @@ __device__ __forceinline__ u32 wave_reserve(u32* counter, u32 c) {
     return base + incl - c;
 }
 
+// As wave_reserve, but never past `cap`: returns kFull (and reserves
+// nothing) when the wave's entries do not fit.  Lock-free CAS by one lane.
+constexpr u32 kFull = 0xFFFFFFFEu;
+__device__ __forceinline__ u32 wave_reserve_cap(u32* counter, u32 c, u32 cap) {
+    const u32 incl = wave_incl_scan(c);
+    const u32 tot = __builtin_amdgcn_readlane(incl, 63);
+    if (tot == 0) return ~0u;
+    u32 base = 0;
+    if (lane_id() == 0) {
+        u32 old = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (;;) {
+            if (old + tot > cap) {
+                base = kFull;
+                break;
+            }
+            const u32 seen = atomicCAS(counter, old, old + tot);
+            if (seen == old) {
+                base = old;
+                break;
+            }
+            old = seen;
+        }
+    }
+    base = __builtin_amdgcn_readfirstlane(base);
+    return base == kFull ? kFull : base + incl - c;
+}
+
 // ------------------------------------------------------------------ block helpers
 // Exclusive prefix sum of one value per thread, in thread order; *total gets
 // the block sum.  Separate consecutive calls by a barrier.
 template <int WG, int CAP>
-__device__ u32 block_excl_scan(Smem<CAP>& sm, u32 v, u32* total) {
+__device__ __forceinline__ u32 block_excl_scan(Smem<CAP>& sm, u32 v, u32* total) {
     const u32 wave = threadIdx.x / kWave;
     const u32 incl = wave_incl_scan(v);
     if (lane_id() == kWave - 1) sm.wsum[wave] = incl;
@@ -210,61 +244,62 @@ __device__ u32 block_excl_scan(Smem<CAP>& sm, u32 v, u32* total) {
     return off + incl - v;
 }
 
-// OR, AND and MIN over the entries of buf[lo, hi) whose bits under `mask`
-// equal `prefix`.  Separate consecutive calls by a barrier.
+constexpr int kBatch = 8;  // LDS loads kept in flight per thread in buffer passes
+
+// MIN and MAX over the entries of buf[lo, hi) whose bits under `mask` equal
+// `prefix` (MIN = ~0, MAX = 0 when none do).  Also zeroes the histogram for
+// the block_hist_find that follows.  Separate consecutive calls by a barrier.
 template <int WG, int CAP>
-__device__ void block_reduce(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, u64& o, u64& a, u64& mn) {
+__device__ __forceinline__ void block_minmax(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, u64& mn, u64& mx) {
     const u32 tid = threadIdx.x;
-    u64 vo = 0, va = ~0ull, vm = ~0ull;
-    for (u32 i = lo + tid; i < hi; i += WG) {
-        const u64 e = sm.buf[i];
-        if ((e & mask) == prefix) {
-            vo |= e;
-            va &= e;
-            vm = e < vm ? e : vm;
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    u64 vmn = ~0ull, vmx = 0;
+    for (u32 base = lo; base < hi; base += WG * kBatch) {
+        u64 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const u32 i = base + u * WG + tid;
+            v[u] = i < hi ? sm.buf[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const u32 i = base + u * WG + tid;
+            if (i < hi && (v[u] & mask) == prefix) {
+                vmn = v[u] < vmn ? v[u] : vmn;
+                vmx = v[u] > vmx ? v[u] : vmx;
+            }
         }
     }
-    vo = wave_or64(vo);
-    va = wave_and64(va);
-    vm = wave_min64(vm);
+    vmn = wave_min64(vmn);
+    vmx = wave_max64(vmx);
     const u32 wave = tid / kWave;
     if (lane_id() == 0) {
-        sm.red[wave][0] = vo;
-        sm.red[wave][1] = va;
-        sm.red[wave][2] = vm;
+        sm.red[wave][0] = vmn;
+        sm.red[wave][1] = vmx;
     }
     __syncthreads();
-    o = 0;
-    a = ~0ull;
     mn = ~0ull;
+    mx = 0;
 #pragma unroll
     for (u32 w = 0; w < WG / kWave; ++w) {
-        o |= sm.red[w][0];
-        a &= sm.red[w][1];
-        mn = sm.red[w][2] < mn ? sm.red[w][2] : mn;
+        mn = sm.red[w][0] < mn ? sm.red[w][0] : mn;
+        mx = sm.red[w][1] > mx ? sm.red[w][1] : mx;
     }
 }
 
-// Histogram of the digit (e >> shift) & (kBins-1) over the entries of
-// buf[lo, hi) matching (prefix, mask); then the bin holding the r-th largest
-// (r >= 1).  Leaves sel_digit, sel_r (rank inside the bin), sel_c (bin size)
-// and sel_above (entries in higher bins) in shared memory.
+// In the filled histogram, the bin holding the r-th largest counted entry
+// (r >= 1), scanning from the highest bin.  Leaves sel_digit, sel_r (rank
+// inside the bin), sel_c (bin size) and sel_above (entries in higher bins) in
+// shared memory; sel_c = 0 when fewer than r entries are counted.
 template <int WG, int CAP>
-__device__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, int shift, u32 r) {
+__device__ __forceinline__ void hist_locate(Smem<CAP>& sm, u32 r) {
     const u32 tid = threadIdx.x;
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
-    if (tid == 0) {  // overwritten below unless r exceeds the matching count
+    if (tid == 0) {  // overwritten below unless fewer than r are counted
         sm.sel_digit = 0;
         sm.sel_r = 0;
         sm.sel_c = 0;
         sm.sel_above = 0;
     }
-    __syncthreads();
-    for (u32 i = lo + tid; i < hi; i += WG) {
-        const u64 e = sm.buf[i];
-        if ((e & mask) == prefix) atomicAdd(&sm.hist[(u32)(e >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
     constexpr int kPer = kBins / WG;  // bins per thread, highest bins first
     u32 h[kPer];
     u32 s = 0;
@@ -275,6 +310,7 @@ __device__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 m
     }
     u32 tot;
     const u32 excl = block_excl_scan<WG, CAP>(sm, s, &tot);
+    if (tid == 0) sm.sel_total = tot;
     if (excl < r && r <= excl + s) {
         u32 acc = excl;
 #pragma unroll
@@ -291,6 +327,29 @@ __device__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 m
     __syncthreads();
 }
 
+// Histogram of the digit (e >> shift) & (kBins-1) over the entries of
+// buf[lo, hi) matching (prefix, mask) -- the histogram must have been zeroed
+// by block_minmax -- then hist_locate(r).
+template <int WG, int CAP>
+__device__ __forceinline__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, int shift, u32 r) {
+    const u32 tid = threadIdx.x;
+    for (u32 base = lo; base < hi; base += WG * kBatch) {
+        u64 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const u32 i = base + u * WG + tid;
+            v[u] = i < hi ? sm.buf[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const u32 i = base + u * WG + tid;
+            if (i < hi && (v[u] & mask) == prefix) atomicAdd(&sm.hist[(u32)(v[u] >> shift) & (kBins - 1)], 1u);
+        }
+    }
+    __syncthreads();
+    hist_locate<WG, CAP>(sm, r);
+}
+
 // Window of kHistBits bits whose top bit is the highest bit set in diff.
 __device__ __forceinline__ int window_shift(u64 diff) {
     const int msb = 63 - __clzll((long long)diff);
@@ -301,28 +360,73 @@ __device__ __forceinline__ u64 bits_above(int shift) {
 }
 
 // ------------------------------------------------------------------ compaction
-// Reduce buf[0, cnt) (distinct composites, cnt > k) to its k largest, in
-// buf[0, k); sets kth (the least kept) and L = kth + 1.
-//
-// Radix select with 11-bit digits.  Each level's window starts at the
-// highest bit where the still-undecided entries differ, so concentrated
-// value distributions still spread over the bins.  After the first level
-// the buffer is partitioned once: entries in higher bins are kept outright,
-// the boundary bin is moved next to them, and later levels only look at that
-// boundary list.  Placement uses block prefix sums, not atomics, so the
-// result order is a deterministic function of the buffer order.
-template <class E, int WG, int CAP>
-__device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k) {
+// Keep the entries of buf[lo, hi) that are >= T, packed from position lo in a
+// deterministic order (block prefix sum).  Returns the kept count.
+template <int WG, int CAP>
+__device__ __forceinline__ u32 keep_at_least(Smem<CAP>& sm, u32 lo, u32 hi, u64 T) {
     const u32 tid = threadIdx.x;
     constexpr int kItems = CAP / WG;
-    u64 o, a, mn;
-    block_reduce<WG, CAP>(sm, 0, cnt, 0ull, 0ull, o, a, mn);
-    int shift = window_shift(o ^ a);
+    u64 mine[kItems];
+    u32 nk = 0;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const u32 i = lo + tid + j * WG;
+        mine[j] = i < hi ? sm.buf[i] : 0ull;
+        nk += (i < hi && mine[j] >= T) ? 1u : 0u;
+    }
+    u32 tot;
+    u32 pk = lo + block_excl_scan<WG, CAP>(sm, nk, &tot);  // its barrier orders reads before writes
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        const u32 i = lo + tid + j * WG;
+        if (i < hi && mine[j] >= T) sm.buf[pk++] = mine[j];
+    }
+    __syncthreads();
+    return tot;
+}
+
+// The r-th largest entry of the undecided set (entries of buf[lo, hi)
+// matching prefix/mask).  Radix select with 11-bit digits whose window
+// starts at the highest bit where the undecided entries differ.
+template <int WG, int CAP>
+__device__ __forceinline__ u64 select_in(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, u32 r) {
+    u64 mn, mx;
+    // Each level fixes at least one more bit; the bound only guards the loop.
+    for (int level = 0; level < 64 / kHistBits + 2; ++level) {
+        block_minmax<WG, CAP>(sm, lo, hi, prefix, mask, mn, mx);
+        if (mn == mx) return mn;  // a single entry left
+        const int shift = window_shift(mn ^ mx);
+        // keep the bits fixed so far: a window clamped at bit 0 can overlap them
+        mask |= bits_above(shift);
+        prefix = mn & mask;
+        block_hist_find<WG, CAP>(sm, lo, hi, prefix, mask, shift, r);
+        const u32 d = sm.sel_digit, c = sm.sel_c, rr = sm.sel_r;
+        prefix |= (u64)d << shift;
+        mask |= (u64)(kBins - 1) << shift;
+        if (rr == c) break;  // the whole bin is kept: the answer is its least entry
+        r = rr;
+    }
+    block_minmax<WG, CAP>(sm, lo, hi, prefix, mask, mn, mx);
+    return mn;
+}
+
+// Reduce buf[0, cnt) (distinct composites, cnt > k) to its k largest, in
+// buf[0, k); sets kth and the bound L to the least kept entry.
+//
+// First level over the whole buffer; then the buffer is partitioned once
+// (entries in higher bins kept outright, the boundary bin moved next to
+// them) and only the boundary list is refined.
+template <class E, int WG, int CAP>
+__device__ __forceinline__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k) {
+    const u32 tid = threadIdx.x;
+    constexpr int kItems = CAP / WG;
+    u64 mn, mx;
+    block_minmax<WG, CAP>(sm, 0, cnt, 0ull, 0ull, mn, mx);
+    const int shift = window_shift(mn ^ mx);
     u64 mask = bits_above(shift);
-    u64 prefix = a & mask;
+    u64 prefix = mn & mask;
     block_hist_find<WG, CAP>(sm, 0, cnt, prefix, mask, shift, k);
-    const u32 b = sm.sel_digit, above = sm.sel_above, c = sm.sel_c;
-    u32 r = sm.sel_r;
+    const u32 b = sm.sel_digit, above = sm.sel_above, c = sm.sel_c, r = sm.sel_r;
 
     // Partition: higher bins to [0, above), bin b to [above, above + c).
     u64 mine[kItems];
@@ -350,53 +454,100 @@ __device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k) {
     mask |= (u64)(kBins - 1) << shift;
 
     const u32 lo = above, hi = above + c;
-    u64 T;
-    if (r == c) {
-        block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
-        T = mn;
-    } else {
-        // Each level fixes at least one more bit, so 64 / kHistBits + 1
-        // levels always suffice; the bound only guards the loop.
-        T = 0;
-        for (int level = 0; level < 64 / kHistBits + 2; ++level) {
-            block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
-            shift = window_shift(o ^ a);
-            // Keep the bits fixed so far: a window clamped at bit 0 can
-            // overlap them.
-            mask |= bits_above(shift);
-            prefix = a & mask;
-            block_hist_find<WG, CAP>(sm, lo, hi, prefix, mask, shift, r);
-            const u32 d2 = sm.sel_digit, c2 = sm.sel_c, r2 = sm.sel_r;
-            prefix |= (u64)d2 << shift;
-            mask |= (u64)(kBins - 1) << shift;
-            if (r2 == c2) {
-                block_reduce<WG, CAP>(sm, lo, hi, prefix, mask, o, a, mn);
-                T = mn;
-                break;
-            }
-            r = r2;
-        }
-        // keep the boundary entries >= T, packed right after the definite ones
-        u32 nk = 0;
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const u32 i = lo + tid + j * WG;
-            mine[j] = i < hi ? sm.buf[i] : 0ull;
-            nk += (i < hi && mine[j] >= T) ? 1u : 0u;
-        }
-        __syncthreads();  // wsum reuse
-        u32 pk = lo + block_excl_scan<WG, CAP>(sm, nk, &tot);
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const u32 i = lo + tid + j * WG;
-            if (i < hi && mine[j] >= T) sm.buf[pk++] = mine[j];
-        }
+    const u64 T = select_in<WG, CAP>(sm, lo, hi, prefix, mask, r);
+    if (r != c) {
+        __syncthreads();
+        keep_at_least<WG, CAP>(sm, lo, hi, T);
     }
     if (tid == 0) {
         sm.count = k;
         sm.kth = T;
-        sm.L = T + 1;
+        // inclusive bound: k entries are >= T, and any later element is
+        // admitted only if it is > T (composites are distinct)
+        sm.L = T;
     }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ histogram-tracked bound
+// The workgroup keeps a histogram of the top kHistBits bits of the value key
+// of every entry it has appended to the buffer (and, for the first tile, of
+// every element of that tile).  The lower edge of the bin holding the k-th
+// counted entry is a valid admission bound: at least k counted elements lie
+// at or above it.  Invariant: for every bin at or above the current bound's
+// bin, the histogram count equals the number of buffer entries in that bin.
+__device__ __forceinline__ u32 top_digit(u64 c) { return (u32)(c >> (64 - kHistBits)); }
+__device__ __forceinline__ u64 digit_floor(u32 d) { return (u64)d << (64 - kHistBits); }
+
+// Recount the buffer into a zeroed histogram (after an exact reduction).
+template <int WG, int CAP>
+__device__ __forceinline__ void rebuild_hist(Smem<CAP>& sm, u32 cnt) {
+    const u32 tid = threadIdx.x;
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    __syncthreads();
+    for (u32 i = tid; i < cnt; i += WG) atomicAdd(&sm.hist[top_digit(sm.buf[i])], 1u);
+    __syncthreads();
+}
+
+// Free room for `room` more entries: drop entries below the histogram
+// bound's bin edge, or, if that is not enough, reduce exactly to k.
+template <class E, int WG, int CAP>
+__device__ __forceinline__ void make_room(Smem<CAP>& sm, u32 cnt, u32 k, u32 room) {
+    const u32 tid = threadIdx.x;
+    hist_locate<WG, CAP>(sm, k);
+    const u32 d = sm.sel_digit, keep = sm.sel_above + sm.sel_c;
+    if (sm.sel_c > 0 && keep + room <= (u32)CAP) {
+        const u32 kept = keep_at_least<WG, CAP>(sm, 0, cnt, digit_floor(d));
+        if (tid == 0) {
+            sm.count = kept;
+            sm.L = digit_floor(d) > sm.L ? digit_floor(d) : sm.L;
+        }
+        __syncthreads();
+        return;
+    }
+    compact_to_k<E, WG, CAP>(sm, cnt, k);
+    rebuild_hist<WG, CAP>(sm, k);
+}
+
+// Reduce the buffer (cnt >= k entries, histogram consistent) to exactly the
+// k largest, in buf[0, k).  The histogram gives the first radix level.
+template <class E, int WG, int CAP>
+__device__ __forceinline__ void final_select(Smem<CAP>& sm, u32 cnt, u32 k) {
+    const u32 tid = threadIdx.x;
+    constexpr int kItems = CAP / WG;
+    if (cnt > k) {
+        hist_locate<WG, CAP>(sm, k);
+        const u32 b = sm.sel_digit, above = sm.sel_above, c = sm.sel_c, r = sm.sel_r;
+        // Partition: higher bins to [0, above), bin b to [above, above + c).
+        u64 mine[kItems];
+        u32 nd = 0, nm = 0;
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const u32 i = tid + j * WG;
+            mine[j] = i < cnt ? sm.buf[i] : 0ull;
+            const u32 d = top_digit(mine[j]);
+            nd += (i < cnt && d > b) ? 1u : 0u;
+            nm += (i < cnt && d == b) ? 1u : 0u;
+        }
+        u32 tot;
+        const u32 ex = block_excl_scan<WG, CAP>(sm, nd | (nm << 16), &tot);  // counts < 2^16
+        u32 pd = ex & 0xFFFFu, pm = above + (ex >> 16);
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const u32 i = tid + j * WG;
+            const u32 d = top_digit(mine[j]);
+            if (i < cnt && d > b) sm.buf[pd++] = mine[j];
+            if (i < cnt && d == b) sm.buf[pm++] = mine[j];
+        }
+        __syncthreads();
+        if (r != c) {
+            const u64 mask = ~0ull << (64 - kHistBits);
+            const u64 T = select_in<WG, CAP>(sm, above, above + c, digit_floor(b), mask, r);
+            __syncthreads();
+            keep_at_least<WG, CAP>(sm, above, above + c, T);
+        }
+    }
+    if (tid == 0) sm.count = k;
     __syncthreads();
 }
 
@@ -405,7 +556,7 @@ __device__ void compact_to_k(Smem<CAP>& sm, u32 cnt, u32 k) {
 // from a bitmap of the selected columns and a prefix popcount over it (when
 // the row's bitmap fits in the free LDS), else from a bitonic sort.
 template <class E, int WG, int CAP>
-__device__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
+__device__ __forceinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
                      void* out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
@@ -489,16 +640,16 @@ struct Params {
     int32_t segs;      // workgroups per row
     int32_t seg_vecs;  // 16-byte vectors per segment
     int32_t n_vec;     // 16-byte vectors per row holding valid columns
-    int32_t idx_bits;  // columns < 2^idx_bits
     uint32_t seed;
     int32_t sorted;
     int32_t retval;
     int32_t* out_idx;
     void* out_val;
-    u64* ws_cand;      // [batch][segs][k]
-    u64* ws_kth;       // [batch][segs]
-    u32* ws_count;     // [batch][segs]
+    u64* ws_cand;      // [batch][segs][pub_cap]: a segment's live candidates, by top digit
+    u64* ws_meta;      // [batch][segs][4]: count | low digit, high digit, bound, q-bound
+    u32* ws_dir;       // [batch][segs][kBins]: entries with top digit >= d, from the low digit
     u32* ws_ticket;    // [batch], zero between calls
+    int32_t pub_cap;   // most candidates a segment publishes
     int32_t* flag;     // set to flag_value when a NaN is seen
     int32_t flag_value;
     int32_t flags;     // kFlag* bits
@@ -522,22 +673,58 @@ __device__ __forceinline__ u32 gcd_u32(u32 a, u32 b) {
     return a;
 }
 
-template <int EB, int WG, int VPT, int CAP>
-__global__ __launch_bounds__(WG) void topk_rows(Params p) {
+// Element slot s of a thread's tile registers: (raw bits, column, valid).
+template <class E, int VPT, int WG>
+struct Slot {
+    static constexpr int kSlots = VPT * E::kPerVec;
+    static constexpr int kPerDword = E::kKeyBits == 16 ? 2 : 1;
+    __device__ static __forceinline__ void get(const uint4 (&v)[VPT], int s, int vb, u32 tid, int v1, u32 n,
+                                               u32& bits, u32& col, bool& valid) {
+        const int j = s / E::kPerVec;
+        const int w = (s % E::kPerVec) / kPerDword;
+        const int hh = s % kPerDword;
+        const u32 d = w == 0 ? v[j].x : w == 1 ? v[j].y : w == 2 ? v[j].z : v[j].w;
+        bits = kPerDword == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
+        const int vi = vb + j * WG + (int)tid;
+        col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
+        valid = vi < v1 && col < n;
+    }
+};
+
+// One workgroup per (row, segment).  EB: element bytes; WG: threads; NV:
+// tiles per chunk (16-byte loads each thread has in flight); CAP:
+// candidate-buffer entries.
+// A "tile" is one vector per thread, WG * 16 bytes; tiles are visited in a
+// pseudo-random order, a chunk at a time.
+template <int EB, int WG, int NV, int CAP>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu((CAP <= 8192 ? 2 : 1) * WG / 256)))
+void topk_rows(Params p) {
     using E = Elem<EB>;
-    constexpr int kTileVecs = WG * VPT;
+    using SL = Slot<E, 1, WG>;
+    constexpr int kTileVecs = WG;
     constexpr int kTileElems = kTileVecs * E::kPerVec;
     static_assert(CAP % WG == 0, "capacity must be a multiple of the workgroup size");
+    static_assert(CAP >= 2 * NV * kTileElems || NV * kTileElems >= 8192, "capacity must hold two chunks");
     __shared__ Smem<CAP> sm;
 
     const u32 tid = threadIdx.x;
     const u32 row = blockIdx.x / (u32)p.segs;
     const u32 seg = blockIdx.x % (u32)p.segs;
     const u32 k = (u32)p.k;
-    const uint4* vin = (const uint4*)(p.in + (int64_t)row * p.row_stride_bytes);
+    const u32 n = (u32)p.n;
+    const uint8_t* row_in = p.in + (int64_t)row * p.row_stride_bytes;
 
     const int v0 = (int)seg * p.seg_vecs;
     const int v1 = min(p.n_vec, v0 + p.seg_vecs);
+    // The segment as a raw buffer resource: loads take one 32-bit offset
+    // (vector index relative to v0, times 16) and the hardware range check
+    // returns zeros past the segment's end instead of faulting.
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(row_in + (int64_t)v0 * 16), (short)0, (int)((u32)(v1 - v0) * 16u), kBufferWord3);
+    auto load_vec = [&](int vi) -> uint4 {  // vi: absolute vector index in the row
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(vi - v0) * 16u, 0, 0);
+        return uint4{r[0], r[1], r[2], r[3]};
+    };
     const u32 ntiles = (u32)((v1 - v0 + kTileVecs - 1) / kTileVecs);
 
     // Tile visiting order: t -> (a t + b) mod ntiles with gcd(a, ntiles) = 1.
@@ -550,106 +737,178 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         b = h % ntiles;
     }
 
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
     if (tid == 0) {
         sm.count = 0;
         sm.L = 0;
-        sm.kth = 0;
         sm.nan = 0;
+        sm.last = 0;
     }
     DSTK_PHASE(0);
-    __syncthreads();
 
     PreFilter<E> pf;
     u64 L = 0;
     pf.set(L);
     bool saw_nan = false;
+    __syncthreads();
 
-    uint4 cur[VPT], nxt[VPT];
-    auto load_tile = [&](uint4 (&v)[VPT], u32 t) {
-        const int vb = v0 + (int)(((u64)a * t + b) % ntiles) * kTileVecs;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int vi = vb + j * WG + (int)tid;
-            v[j] = vi < v1 ? vin[vi] : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
+    u32 pr = b;  // permuted index of the next tile to request
+    constexpr int kSeed = NV < 2 ? NV : 2;  // tiles counted to seed the bound
+    static_assert(CAP >= kSeed * kTileElems, "the seed tiles must fit an empty buffer");
 
-    load_tile(cur, 0);
-    for (u32 t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_tile(nxt, t + 1);
-        const int vb = v0 + (int)(((u64)a * t + b) % ntiles) * kTileVecs;
-        u32 any = 0;
+    // Filter one tile (one vector per thread) against the bound, appending
+    // admitted elements and counting them in the histogram.  Returns false,
+    // appending nothing, when the wave's admitted elements do not fit.
+    auto filter = [&](const uint4& x, int vbi) -> bool {
+        const u32 any = pf.any(x.x) | pf.any(x.y) | pf.any(x.z) | pf.any(x.w);
+        if (__ballot(any != 0) == 0) return true;
+        const uint4 xs[1] = {x};
+        u32 pm = 0, c = 0;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            any |= pf.any(cur[j].x) | pf.any(cur[j].y) | pf.any(cur[j].z) | pf.any(cur[j].w);
+        for (int s = 0; s < SL::kSlots; ++s) {
+            u32 bits, col;
+            bool valid;
+            SL::get(xs, s, vbi, tid, v1, n, bits, col, valid);
+            saw_nan |= valid && E::is_nan(bits);
+            const bool ok = valid && compose<E>(E::key(bits), col) >= L;
+            pm |= (u32)ok << s;
+            c += ok;
         }
-        if (__ballot(any != 0) != 0) {
-            // Exact test on every element slot; one LDS reservation per wave.
-            constexpr int kSlots = VPT * E::kPerVec;
-            constexpr int kPerDword = EB == 2 ? 2 : 1;
-            u32 pm = 0, c = 0;
+        u32 pos = wave_reserve_cap(&sm.count, c, (u32)CAP);
+        if (pos == kFull) return false;
+        if (pos != ~0u) {
 #pragma unroll
-            for (int s = 0; s < kSlots; ++s) {
-                const int j = s / E::kPerVec;
-                const int w = (s % E::kPerVec) / kPerDword;
-                const int hh = s % kPerDword;
-                const u32 d = w == 0 ? cur[j].x : w == 1 ? cur[j].y : w == 2 ? cur[j].z : cur[j].w;
-                const u32 bits = EB == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
-                const int vi = vb + j * WG + (int)tid;
-                const u32 col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
-                const bool valid = vi < v1 && col < (u32)p.n;
-                saw_nan |= valid && E::is_nan(bits);
-                const bool ok = valid && compose<E>(E::key(bits), col) >= L;
-                pm |= (u32)ok << s;
-                c += ok;
-            }
-            u32 pos = wave_reserve(&sm.count, c);
-            if (pos != ~0u) {
-#pragma unroll
-                for (int s = 0; s < kSlots; ++s) {
-                    if ((pm >> s) & 1u) {
-                        const int j = s / E::kPerVec;
-                        const int w = (s % E::kPerVec) / kPerDword;
-                        const int hh = s % kPerDword;
-                        const u32 d = w == 0 ? cur[j].x : w == 1 ? cur[j].y : w == 2 ? cur[j].z : cur[j].w;
-                        const u32 bits = EB == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
-                        const int vi = vb + j * WG + (int)tid;
-                        const u32 col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
-                        sm.buf[pos++] = compose<E>(E::key(bits), col);
-                    }
+            for (int s = 0; s < SL::kSlots; ++s) {
+                if ((pm >> s) & 1u) {
+                    u32 bits, col;
+                    bool valid;
+                    SL::get(xs, s, vbi, tid, v1, n, bits, col, valid);
+                    const u64 e = compose<E>(E::key(bits), col);
+                    sm.buf[pos++] = e;
+                    atomicAdd(&sm.hist[top_digit(e)], 1u);
                 }
             }
         }
-        __syncthreads();
-        const u32 cnt = sm.count;
-        if (cnt > (u32)(CAP - kTileElems)) {
-            compact_to_k<E, WG, CAP>(sm, cnt, k);
-            L = sm.L;
+        return true;
+    };
+
+    // Phase A, per chunk of NV tiles: all NV loads requested at once and
+    // filtered in request order (straight-line code, so each tile waits only
+    // for its own load; lanes past the segment read zeros and are masked out).  After the seed, filtering
+    // takes no workgroup barrier: waves run independently and hide each
+    // other's load latency.  A wave whose entries do not fit records the
+    // tile; phase B makes room and filters those tiles again.
+    for (u32 t0 = 0; t0 < ntiles; t0 += NV) {
+        uint4 v[NV];
+        int vb[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            vb[i] = t0 + (u32)i < ntiles ? v0 + (int)pr * kTileVecs : v1;
+            v[i] = load_vec(vb[i] + (int)tid);
+            __builtin_amdgcn_sched_barrier(0);  // keep requests in slot order
+            pr += a;
+            if (pr >= ntiles) pr -= ntiles;
+        }
+        u32 pending = 0;  // wave-uniform: tiles this wave still has to append
+        if (t0 == 0) {
+            // Seed: count every element of the first kSeed tiles, take the
+            // bin edge of the k-th counted as the bound, then admit those
+            // tiles' elements at or above it (they always fit).
+#pragma unroll
+            for (int i = 0; i < kSeed; ++i) {
+                const uint4 xs[1] = {v[i]};
+#pragma unroll
+                for (int s = 0; s < SL::kSlots; ++s) {
+                    u32 bits, col;
+                    bool valid;
+                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                    if (valid) {
+                        saw_nan |= E::is_nan(bits);
+                        atomicAdd(&sm.hist[top_digit(compose<E>(E::key(bits), col))], 1u);
+                    }
+                }
+            }
+            __syncthreads();
+            hist_locate<WG, CAP>(sm, k);
+            if (sm.sel_c > 0) L = digit_floor(sm.sel_digit);
+            pf.set(L);
+#pragma unroll
+            for (int i = 0; i < kSeed; ++i) {
+                const uint4 xs[1] = {v[i]};
+                u32 pm = 0, c = 0;
+#pragma unroll
+                for (int s = 0; s < SL::kSlots; ++s) {
+                    u32 bits, col;
+                    bool valid;
+                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                    const bool ok = valid && compose<E>(E::key(bits), col) >= L;
+                    pm |= (u32)ok << s;
+                    c += ok;
+                }
+                u32 pos = wave_reserve(&sm.count, c);
+                if (pos != ~0u) {
+#pragma unroll
+                    for (int s = 0; s < SL::kSlots; ++s) {
+                        if ((pm >> s) & 1u) {
+                            u32 bits, col;
+                            bool valid;
+                            SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                            sm.buf[pos++] = compose<E>(E::key(bits), col);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = kSeed; i < NV; ++i)
+                if (!filter(v[i], vb[i])) pending |= 1u << i;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (!filter(v[i], vb[i])) pending |= 1u << i;
+        }
+
+        // Phase B (rare): make room, raise the bound, filter what did not fit.
+        for (int round = 0; round < 64; ++round) {
+            __syncthreads();
+            if (lane_id() == 0 && pending) atomicOr(&sm.last, 1u);
+            __syncthreads();
+            const bool again = sm.last != 0;
+            __syncthreads();
+            if (!again) break;
+            if (tid == 0) sm.last = 0;
+            make_room<E, WG, CAP>(sm, sm.count, k, kTileElems);
+            hist_locate<WG, CAP>(sm, k);
+            if (sm.sel_c > 0 && digit_floor(sm.sel_digit) > L) L = digit_floor(sm.sel_digit);
+            if (sm.L > L) L = sm.L;
+            pf.set(L);
+            const u32 todo = pending;
+            pending = 0;
+            for (int i = 0; i < NV; ++i) {
+                if ((todo >> i) & 1u) {
+                    const uint4 x = load_vec(vb[i] + (int)tid);  // cached: read moments ago
+                    if (!filter(x, vb[i])) pending |= 1u << i;
+                }
+            }
+        }
+        // Between chunks (long segments only): tidy up and raise the bound.
+        if (t0 + NV < ntiles) {
+            if (sm.count > (u32)CAP / 2) make_room<E, WG, CAP>(sm, sm.count, k, 0);
+            hist_locate<WG, CAP>(sm, k);
+            if (sm.sel_c > 0 && digit_floor(sm.sel_digit) > L) L = digit_floor(sm.sel_digit);
+            if (sm.L > L) L = sm.L;
             pf.set(L);
         }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) cur[j] = nxt[j];
     }
-
-    DSTK_PHASE(1);
-    // Final reduction of this segment to at most k entries.
-    u32 cnt = sm.count;
-    if (cnt > k) {
-        compact_to_k<E, WG, CAP>(sm, cnt, k);
-        cnt = k;
-    } else if (cnt == k && p.segs > 1) {
-        // k-th = least entry; a valid lower bound for the whole row
-        u64 o, a, mn;
-        block_reduce<WG, CAP>(sm, 0, cnt, 0ull, 0ull, o, a, mn);
-        if (tid == 0) sm.kth = mn;
-        __syncthreads();
-    }
-    DSTK_PHASE(2);
-
     if (saw_nan) sm.nan = 1;  // benign race: every writer stores 1
+    if (tid == 0) sm.L = L;
+    DSTK_PHASE(1);
+    __syncthreads();
+    u32 cnt = sm.count;
 
     if (p.segs == 1) {
-        emit<E, WG, CAP>(sm, k, (u32)p.n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
+        final_select<E, WG, CAP>(sm, cnt, k);
+        DSTK_PHASE(2);
+        emit<E, WG, CAP>(sm, k, n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
                          p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
         __syncthreads();
         if (tid == 0 && sm.nan) *p.flag = p.flag_value;
@@ -657,21 +916,88 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         return;
     }
 
-    // ---- split row: publish this segment's survivors, last arriver merges
-    const u32 slot = row * (u32)p.segs + seg;
-    u64* cand = p.ws_cand + (u64)slot * k;
-    for (u32 i = tid; i < cnt; i += WG) cand[i] = sm.buf[i];
-    if (tid == 0) {
-        p.ws_count[slot] = cnt;
-        p.ws_kth[slot] = cnt == k ? sm.kth : 0ull;
+    // ---- split row: publish this segment's live candidates, sorted by top
+    // digit, with a directory of cumulative counts per digit.
+    const u32 S = (u32)p.segs;
+    const u32 slot = row * S + seg;
+    {
+        // bound for rank q = ceil(k / S): with every segment's list holding
+        // q entries at or above its own such bound, the smallest of them is
+        // a valid bound for the row
+        const u32 q = (k + S - 1) / S;
+        hist_locate<WG, CAP>(sm, q);
+        const u64 bq = sm.sel_c > 0 ? digit_floor(sm.sel_digit) : 0ull;
+        hist_locate<WG, CAP>(sm, k);
+        u32 dl = sm.sel_c > 0 ? sm.sel_digit : 0u;
+        u32 live = sm.sel_c > 0 ? sm.sel_above + sm.sel_c : sm.sel_total;
+        if (live > (u32)p.pub_cap) {
+            // too many to publish: reduce this segment exactly to k first
+            compact_to_k<E, WG, CAP>(sm, cnt, k);
+            rebuild_hist<WG, CAP>(sm, k);
+            cnt = k;
+            hist_locate<WG, CAP>(sm, k);
+            dl = sm.sel_digit;
+            live = sm.sel_above + sm.sel_c;
+            if (L < sm.L) L = sm.L;
+        }
+        // hist[d] -> number of live entries in higher bins (for d >= dl);
+        // directory: entries with digit >= d, written for d in [dl, d_hi]
+        constexpr int kPer = kBins / WG;
+        u32 hv[kPer];
+        u32 sum = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const u32 d = kBins - 1 - tid * kPer - j;
+            hv[j] = d >= dl ? sm.hist[d] : 0u;
+            sum += hv[j];
+        }
+        u32 tot;
+        u32 run = block_excl_scan<WG, CAP>(sm, sum, &tot);
+        u32* dir = p.ws_dir + (u64)slot * kBins;
+        if (run == 0 && sum > 0) {
+#pragma unroll
+            for (int j = kPer - 1; j >= 0; --j)
+                if (hv[j]) sm.d_hi = kBins - 1 - tid * kPer - j;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const u32 d = kBins - 1 - tid * kPer - j;
+            if (d >= dl) {
+                sm.hist[d] = run;
+                run += hv[j];
+                if (run > 0) dir[d - dl] = run;
+            }
+        }
+        __syncthreads();
+        u64* cand = p.ws_cand + (u64)slot * (u32)p.pub_cap;
+        constexpr int kItems = CAP / WG;
+        u64 mine[kItems];
+        u32 at[kItems];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const u32 i = tid + j * WG;
+            mine[j] = i < cnt ? sm.buf[i] : 0ull;
+            at[j] = (i < cnt && top_digit(mine[j]) >= dl) ? atomicAdd(&sm.hist[top_digit(mine[j])], 1u) : ~0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kItems; ++j)
+            if (at[j] != ~0u) cand[at[j]] = mine[j];
+        if (tid == 0) {
+            u64* meta = p.ws_meta + (u64)slot * 4;
+            meta[0] = (u64)live | ((u64)dl << 32);
+            meta[1] = (u64)(live ? sm.d_hi : 0u);
+            meta[2] = L;
+            meta[3] = bq;
+        }
     }
+    DSTK_PHASE(2);
     __syncthreads();
     if (tid == 0) {
         // release this workgroup's stores (ordered before by the barrier) to
         // the device, then take a ticket; the last ticket merges
         __threadfence();
         const u32 prev = atomicAdd(&p.ws_ticket[row], 1u);
-        sm.last = prev == (u32)p.segs - 1;
+        sm.last = prev == S - 1;
         if (sm.last) __threadfence();
     }
     __syncthreads();
@@ -682,33 +1008,57 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
     }
     DSTK_PHASE(4);
 
-    // Merge: every element of the row's top-k is in some segment's list, and
-    // no segment's k-th composite exceeds the row's k-th, so the largest of
-    // them is a valid admission bound.
-    const u32 S = (u32)p.segs;
-    const u64* rc = p.ws_cand + (u64)row * S * k;
-    for (u32 s = tid; s < S; s += WG) sm.seg_count[s] = p.ws_count[row * S + s];
-    if (tid < kWave) {
-        u64 mx = 0;
-        for (u32 s = tid; s < S; s += kWave) {
-            const u64 v = p.ws_kth[row * S + s];
-            mx = v > mx ? v : mx;
+    // Merge.  Every element of the row's top-k is among some segment's live
+    // list.  Bounds: a segment with at least k elements has k of them at or
+    // above its bound; every segment has q = ceil(k/S) at or above its
+    // q-bound, so the smallest q-bound over the row is valid as well.
+    const u32 cap = (u32)p.pub_cap;
+    const u64* rc = p.ws_cand + (u64)row * S * cap;
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    {
+        u64 m0 = 0, m1 = 0, m2 = 0, m3 = ~0ull;
+        if (tid < S) {
+            const u64* meta = p.ws_meta + (u64)(row * S + tid) * 4;
+            m0 = meta[0];
+            m1 = meta[1];
+            m2 = meta[2];
+            m3 = meta[3];
         }
+        // row bound: max over segment bounds, max with min over q-bounds
+        u64 vmax = wave_max64(m2), vmin = wave_min64(m3);
+        const u32 wave = tid / kWave;
+        if (lane_id() == 0) {
+            sm.red[wave][0] = vmax;
+            sm.red[wave][1] = vmin;
+        }
+        __syncthreads();
+        u64 lmax = 0, qmin = ~0ull;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const u64 t = __shfl_xor(mx, o, kWave);
-            mx = t > mx ? t : mx;
+        for (u32 w = 0; w < WG / kWave; ++w) {
+            lmax = sm.red[w][0] > lmax ? sm.red[w][0] : lmax;
+            qmin = sm.red[w][1] < qmin ? sm.red[w][1] : qmin;
         }
+        L = lmax > qmin ? lmax : qmin;
+        const u32 df = top_digit(L);
+        u32 m = 0;
+        if (tid < S) {
+            const u32 live = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)m1;
+            if (live == 0 || df > dh) m = 0;
+            else if (df <= dl) m = live;
+            else m = p.ws_dir[(u64)(row * S + tid) * kBins + (df - dl)];
+        }
+        u32 total;
+        const u32 off = block_excl_scan<WG, CAP>(sm, m, &total);
+        if (tid < S) sm.seg_count[tid] = off;
         if (tid == 0) {
-            sm.L = mx;
+            sm.newtotal = total;
             sm.count = 0;
             p.ws_ticket[row] = 0;  // ready for the next call
         }
+        __syncthreads();
     }
-    __syncthreads();
-    L = sm.L;
+    const u32 total = sm.newtotal;
     constexpr int kMI = kTileElems / WG;  // merge entries per thread per step
-    const u32 total = S * k;
     for (u32 base = 0; base < total; base += WG * kMI) {
         u64 e[kMI];
         u32 pm = 0, c = 0;
@@ -717,10 +1067,14 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
             const u32 f = base + j * WG + tid;
             e[j] = 0;
             if (f < total) {
-                const u32 s = f / k, jj = f - s * k;
-                if (jj < sm.seg_count[s]) e[j] = rc[f];
+                u32 lo = 0, hi = S;  // last segment whose offset is <= f
+                while (hi - lo > 1) {
+                    const u32 mid = (lo + hi) >> 1;
+                    if (sm.seg_count[mid] <= f) lo = mid; else hi = mid;
+                }
+                e[j] = rc[(u64)lo * cap + (f - sm.seg_count[lo])];
             }
-            const bool ok = e[j] != 0 && e[j] >= L;  // composites of real elements are nonzero
+            const bool ok = f < total && e[j] >= L;
             pm |= (u32)ok << j;
             c += ok;
         }
@@ -728,19 +1082,19 @@ __global__ __launch_bounds__(WG) void topk_rows(Params p) {
         if (pos != ~0u) {
 #pragma unroll
             for (int j = 0; j < kMI; ++j)
-                if ((pm >> j) & 1u) sm.buf[pos++] = e[j];
+                if ((pm >> j) & 1u) {
+                    sm.buf[pos++] = e[j];
+                    atomicAdd(&sm.hist[top_digit(e[j])], 1u);
+                }
         }
         __syncthreads();
         const u32 c2 = sm.count;
-        if (c2 > (u32)(CAP - kTileElems)) {
-            compact_to_k<E, WG, CAP>(sm, c2, k);
-            L = sm.L;
-        }
+        if (c2 > (u32)(CAP - kTileElems)) make_room<E, WG, CAP>(sm, c2, k, kTileElems);
     }
     cnt = sm.count;
-    if (cnt > k) compact_to_k<E, WG, CAP>(sm, cnt, k);
+    final_select<E, WG, CAP>(sm, cnt, k);
     DSTK_PHASE(5);
-    emit<E, WG, CAP>(sm, k, (u32)p.n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
+    emit<E, WG, CAP>(sm, k, n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
                      p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
     __syncthreads();
     if (tid == 0 && sm.nan) *p.flag = p.flag_value;

@@ -115,7 +115,10 @@ def test_plans_for_workloads(pkg, cfg):
     n_vec = -(-c["n"] // epv)
     assert 1 <= p.segments <= 256
     assert p.segments * p.segment_vectors >= n_vec > (p.segments - 1) * p.segment_vectors
-    assert p.capacity >= c["k"] + p.threads * p.vectors_per_tile_thread * epv
+    tile = p.threads * epv  # elements in one tile (one 16-byte vector per thread)
+    assert p.tiles_per_chunk >= 1
+    assert p.capacity >= 2 * tile  # the two seed tiles fit an empty buffer
+    assert p.capacity >= c["k"] + tile  # k kept plus a tile appended
     assert p.grid == c["batch"] * p.segments
     if p.segments > 1:
         assert p.workspace_bytes >= c["batch"] * p.segments * c["k"] * 8
