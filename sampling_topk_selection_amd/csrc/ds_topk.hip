@@ -21,7 +21,10 @@ constexpr int kVersion = 100;       // 0.1.0
 constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS count each)
 constexpr int kTargetWG = 512;      // about two workgroups per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
-constexpr int kLoadsPerThread = 4;  // tiles per chunk: 16-byte loads each thread has in flight
+#ifndef DS_TOPK_TILES_PER_CHUNK
+#define DS_TOPK_TILES_PER_CHUNK 4
+#endif
+constexpr int kLoadsPerThread = DS_TOPK_TILES_PER_CHUNK;  // tiles per chunk: 16-byte loads in flight per thread
 constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
 
 thread_local std::string g_err;

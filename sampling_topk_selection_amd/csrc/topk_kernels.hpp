@@ -116,6 +116,12 @@ constexpr int kHistBits = 11;  // radix-select digit width
 constexpr int kBins = 1 << kHistBits;
 constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
 
+// Histogram storage is transposed: bin d lives at ((d mod 32) * 64 + d / 32),
+// so the 32 consecutive bins one lane owns in wave_locate form a column that
+// it reads with immediate offsets from one address, and a row of 64 lanes
+// hits 64 consecutive words (no bank conflicts).
+__device__ __forceinline__ u32 hidx(u32 d) { return ((d & 31u) << 6) | (d >> 5); }
+
 template <int CAP>
 struct Smem {
     u64 buf[CAP];      // candidate composites
@@ -131,11 +137,26 @@ struct Smem {
     u32 last;
     u32 newtotal;
     u32 seg_count[256];  // merge: offset of each segment's list
+    // wave_locate results, for up to two ranks
+    u32 loc_digit[2], loc_r[2], loc_c[2], loc_above[2];
+    u32 loc_total, loc_dhi;
+    u32 outcount;        // emit: output slots handed out
+    u32 pflag[2];        // scan: "some wave has a tile left over", two slots
+    u32 tbase[512];      // emit: per-thread base rank in the column bitmap
+#ifdef DSTK_PROBE_SLOTS
+    u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
+#endif
 };
 
 // Optional instrumentation hook (phase timestamps); compiled out by default.
 #ifndef DSTK_PHASE
 #define DSTK_PHASE(i) ((void)0)
+#endif
+#ifndef DSTK_PROBE_INIT
+#define DSTK_PROBE_INIT
+#endif
+#ifndef DSTK_PROBE_FLUSH
+#define DSTK_PROBE_FLUSH() ((void)0)
 #endif
 
 // ------------------------------------------------------------------ wave helpers
@@ -172,6 +193,8 @@ __device__ __forceinline__ u32 wave_incl_scan(u32 x) {
     }
 DSTK_WAVE_REDUCE(wave_min, (t < v ? t : v), 0xFFFFFFFFu)
 DSTK_WAVE_REDUCE(wave_max, (t > v ? t : v), 0u)
+DSTK_WAVE_REDUCE(wave_or, (t | v), 0u)
+DSTK_WAVE_REDUCE(wave_and, (t & v), 0xFFFFFFFFu)
 #undef DSTK_WAVE_REDUCE
 
 __device__ __forceinline__ u64 wave_min64(u64 v) {
@@ -183,6 +206,20 @@ __device__ __forceinline__ u64 wave_max64(u64 v) {
     const u32 hi = wave_max((u32)(v >> 32));
     const u32 lo = wave_max((u32)(v >> 32) == hi ? (u32)v : 0u);
     return ((u64)hi << 32) | lo;
+}
+
+// Device-coherent (agent scope) stores and loads.  On gfx950 these are plain
+// vector memory ops with the device-scope cache policy: stores go through to
+// the device-coherent level, loads do not hit a stale L2 line.  Data handed
+// from one workgroup to another goes through these, so the hand-off needs no
+// release fence (which would write back the whole L2).
+template <class T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Reserve `c` consecutive slots per lane behind *counter (one LDS atomic per
@@ -305,7 +342,7 @@ __device__ __forceinline__ void hist_locate(Smem<CAP>& sm, u32 r) {
     u32 s = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        h[j] = sm.hist[kBins - 1 - tid * kPer - j];
+        h[j] = sm.hist[hidx(kBins - 1 - tid * kPer - j)];
         s += h[j];
     }
     u32 tot;
@@ -343,7 +380,7 @@ __device__ __forceinline__ void block_hist_find(Smem<CAP>& sm, u32 lo, u32 hi, u
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const u32 i = base + u * WG + tid;
-            if (i < hi && (v[u] & mask) == prefix) atomicAdd(&sm.hist[(u32)(v[u] >> shift) & (kBins - 1)], 1u);
+            if (i < hi && (v[u] & mask) == prefix) atomicAdd(&sm.hist[hidx((u32)(v[u] >> shift) & (kBins - 1))], 1u);
         }
     }
     __syncthreads();
@@ -485,14 +522,14 @@ __device__ __forceinline__ void rebuild_hist(Smem<CAP>& sm, u32 cnt) {
     const u32 tid = threadIdx.x;
     for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
     __syncthreads();
-    for (u32 i = tid; i < cnt; i += WG) atomicAdd(&sm.hist[top_digit(sm.buf[i])], 1u);
+    for (u32 i = tid; i < cnt; i += WG) atomicAdd(&sm.hist[hidx(top_digit(sm.buf[i]))], 1u);
     __syncthreads();
 }
 
 // Free room for `room` more entries: drop entries below the histogram
 // bound's bin edge, or, if that is not enough, reduce exactly to k.
 template <class E, int WG, int CAP>
-__device__ __forceinline__ void make_room(Smem<CAP>& sm, u32 cnt, u32 k, u32 room) {
+__device__ __noinline__ void make_room(Smem<CAP>& sm, u32 cnt, u32 k, u32 room) {
     const u32 tid = threadIdx.x;
     hist_locate<WG, CAP>(sm, k);
     const u32 d = sm.sel_digit, keep = sm.sel_above + sm.sel_c;
@@ -512,7 +549,7 @@ __device__ __forceinline__ void make_room(Smem<CAP>& sm, u32 cnt, u32 k, u32 roo
 // Reduce the buffer (cnt >= k entries, histogram consistent) to exactly the
 // k largest, in buf[0, k).  The histogram gives the first radix level.
 template <class E, int WG, int CAP>
-__device__ __forceinline__ void final_select(Smem<CAP>& sm, u32 cnt, u32 k) {
+__device__ __noinline__ void final_select(Smem<CAP>& sm, u32 cnt, u32 k) {
     const u32 tid = threadIdx.x;
     constexpr int kItems = CAP / WG;
     if (cnt > k) {
@@ -556,7 +593,7 @@ __device__ __forceinline__ void final_select(Smem<CAP>& sm, u32 cnt, u32 k) {
 // from a bitmap of the selected columns and a prefix popcount over it (when
 // the row's bitmap fits in the free LDS), else from a bitonic sort.
 template <class E, int WG, int CAP>
-__device__ __forceinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
+__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
                      void* out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
@@ -631,6 +668,241 @@ __device__ __forceinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, in
     }
 }
 
+// ------------------------------------------------------------------ selection by threshold
+__device__ __forceinline__ u64 low_mask(int b) { return b >= 64 ? ~0ull : ((1ull << b) - 1ull); }
+
+// Run by one whole wave while the others wait at the caller's next barrier.
+// Lane l owns histogram bins [kBins - 32 (l + 1), kBins - 32 l), so lane 0
+// holds the highest.  For ranks r0 and r1 (r >= 1; 0 = not wanted) it finds
+// the bin holding the r-th largest counted entry and leaves loc_digit,
+// loc_r (rank inside the bin), loc_c (bin count, 0 when fewer than r are
+// counted) and loc_above (entries in higher bins); also loc_total and
+// loc_dhi (highest non-empty bin).  zero: clear the histogram afterwards.
+template <int CAP>
+__device__ __noinline__ void wave_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero) {
+    const u32 l = lane_id();
+    u32* hc = sm.hist + (63u - l);  // this lane's bins, kBins - 32 (l + 1) + j, at hc[64 j]
+    u32 s = 0;
+#pragma unroll
+    for (u32 j = 0; j < 32; ++j) s += hc[64 * j];
+    const u32 incl = wave_incl_scan(s);
+    const u32 excl = incl - s;
+    if (l == 63) sm.loc_total = incl;
+    // Second step inside one lane's 32 bins, spread over the wave: lane i
+    // (< 32) takes bin lo(f) + 31 - i, so lane order is descending bin order.
+    const u32 i32 = l & 31u;
+    const u64 nz = __ballot(s != 0);
+    if (nz == 0) {
+        if (l == 0) sm.loc_dhi = 0;
+    } else {
+        const u32 f = (u32)__builtin_ctzll(nz);
+        const u32 flo = kBins - 32u * (f + 1u);
+        const u32 c = l < 32 ? sm.hist[hidx(flo + 31u - i32)] : 0u;
+        const u64 m = __ballot(c != 0);
+        if (l == 0) sm.loc_dhi = flo + 31u - (u32)__builtin_ctzll(m);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const u32 r = q == 0 ? r0 : r1;
+        if (r == 0) continue;
+        const u64 m = __ballot(excl < r && r <= incl);
+        if (m == 0) {
+            if (l == 0) {
+                sm.loc_digit[q] = 0;
+                sm.loc_r[q] = 0;
+                sm.loc_c[q] = 0;
+                sm.loc_above[q] = 0;
+            }
+            continue;
+        }
+        const u32 f = (u32)__builtin_ctzll(m);
+        const u32 flo = kBins - 32u * (f + 1u);
+        const u32 base = __builtin_amdgcn_readlane(excl, f);
+        const u32 c = l < 32 ? sm.hist[hidx(flo + 31u - i32)] : 0u;
+        const u32 ci = wave_incl_scan(c);  // lanes >= 32 add nothing
+        const u32 ce = base + ci - c;      // entries in higher bins
+        const u64 hit = __ballot(l < 32 && ce < r && r <= ce + c);
+        if (l == (u32)__builtin_ctzll(hit)) {
+            sm.loc_digit[q] = flo + 31u - i32;
+            sm.loc_r[q] = r - ce;
+            sm.loc_c[q] = c;
+            sm.loc_above[q] = ce;
+        }
+    }
+    if (zero) {
+#pragma unroll
+        for (u32 j = 0; j < 32; ++j) hc[64 * j] = 0;
+    }
+}
+
+// The threshold T with exactly k entries of buf[0, cnt) at or above it,
+// given the top-digit bin b1 that holds the k-th largest entry, the rank r1
+// inside it and its size c1.  Radix refinement inside the bin: 11-bit
+// digits, each window starting at the highest bit where the remaining
+// entries can still differ (taken from the OR and AND of the bin's
+// entries), so runs of bits shared by all of them (equal values, the high
+// bits of small column numbers) cost no level.  The histogram must be zero
+// on entry and is zero again on return.
+template <int WG, int CAP>
+__device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1) {
+    if (r1 >= c1) return digit_floor(b1);  // the whole bin is kept
+    const u32 tid = threadIdx.x, wave = tid / kWave;
+    constexpr int kTop = 64 - kHistBits;
+    u64 o = 0, a = ~0ull;
+    for (u32 i = tid; i < cnt; i += WG) {
+        const u64 e = sm.buf[i];
+        if (top_digit(e) == b1) {
+            o |= e;
+            a &= e;
+        }
+    }
+    {
+        const u32 ohi = wave_or((u32)(o >> 32)), olo = wave_or((u32)o);
+        const u32 ahi = wave_and((u32)(a >> 32)), alo = wave_and((u32)a);
+        if (lane_id() == 0) {
+            sm.red[wave][0] = ((u64)ohi << 32) | olo;
+            sm.red[wave][1] = ((u64)ahi << 32) | alo;
+        }
+    }
+    __syncthreads();
+    u64 O = 0, A = ~0ull;
+#pragma unroll
+    for (u32 w = 0; w < WG / kWave; ++w) {
+        O |= sm.red[w][0];
+        A &= sm.red[w][1];
+    }
+    u64 D = (O ^ A) & low_mask(kTop);  // bits where entries of the bin differ
+    DSTK_PHASE(20);
+    u64 P = digit_floor(b1);           // bits fixed so far (above `fixed`)
+    int fixed = kTop;
+    u32 r = r1;
+    for (int level = 0; level < 64 / kHistBits + 2; ++level) {
+        // D != 0 here: the remaining set has at least two (distinct) entries
+        const int hb = 63 - __clzll((long long)D);
+        const int sh = hb >= kHistBits - 1 ? hb - (kHistBits - 1) : 0;
+        P |= A & (low_mask(fixed) & ~low_mask(hb + 1));  // bits shared by the whole set
+        const u64 pm = ~low_mask(hb + 1);
+        for (u32 i = tid; i < cnt; i += WG) {
+            const u64 e = sm.buf[i];
+            if ((e & pm) == P) atomicAdd(&sm.hist[hidx((u32)(e >> sh) & (kBins - 1))], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_locate(sm, r, 0u, true);
+        __syncthreads();
+        const u32 d = sm.loc_digit[0], rr = sm.loc_r[0], c = sm.loc_c[0];
+        P |= (u64)d << sh;
+        DSTK_PHASE(21);
+        fixed = sh;
+        if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
+        r = rr;
+        D &= low_mask(sh);
+    }
+    return P;
+}
+
+// Compact the entries >= T to buf[0, k) and write them with emit() (index
+// order by a bitmap behind them, or a bitonic sort).
+template <class E, int WG, int CAP>
+__device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
+                                            int flags, int32_t* out_idx, void* out_val) {
+    __syncthreads();
+    keep_at_least<WG, CAP>(sm, 0, cnt, T);
+    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx, out_val);
+}
+
+// Reduce buf[0, cnt) exactly to its k largest (b1/r1/c1 locate the k-th in
+// the histogram), rebuild the histogram and locate ranks k and q again.
+// Returns the new count; sm.kth gets the k-th entry.
+template <int WG, int CAP>
+__device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u32 b1, u32 r1, u32 c1) {
+    const u32 tid = threadIdx.x;
+    __syncthreads();
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    __syncthreads();
+    const u64 T = refine<WG, CAP>(sm, cnt, b1, r1, c1);
+    __syncthreads();
+    cnt = keep_at_least<WG, CAP>(sm, 0, cnt, T);
+    if (tid == 0) sm.kth = T;
+    rebuild_hist<WG, CAP>(sm, cnt);
+    if (tid / kWave == 0) wave_locate(sm, k, q, false);
+    __syncthreads();
+    return cnt;
+}
+
+// Write the k entries of buf[0, cnt) that are >= T.  Unordered: one slot
+// reservation per wave.  Index order: a bitmap of the selected columns (in
+// the free histogram, or behind the entries) and a prefix popcount over it;
+// when no bitmap fits, compact and fall back to emit().
+template <class E, int WG, int CAP>
+__device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
+                                               int flags, int32_t* out_idx, void* out_val) {
+    const u32 tid = threadIdx.x;
+    using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
+    VT* ov = (VT*)out_val;
+    if (!sorted) {
+        u32 mine = 0;
+        for (u32 i = tid; i < cnt; i += WG) mine += sm.buf[i] >= T ? 1u : 0u;
+        u32 pos = wave_reserve(&sm.outcount, mine);
+        if (mine == 0) return;
+        for (u32 i = tid; i < cnt; i += WG) {
+            const u64 e = sm.buf[i];
+            if (e >= T) {
+                if (pos < k) {
+                    out_idx[pos] = (int32_t)comp_col<E>(e);
+                    if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
+                }
+                ++pos;
+            }
+        }
+        return;
+    }
+    const u32 words = (n + 31) / 32;
+    u32* bm = nullptr;
+    DSTK_PHASE(22);
+    if (!(flags & kFlagBitonic)) {
+        if (words <= (u32)kBins) bm = sm.hist;
+        else if ((u64)cnt * 2 + words <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
+    }
+    if (!bm) {
+        emit_compacted<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, out_idx, out_val);
+        return;
+    }
+    __syncthreads();  // the histogram may still be read by the last locate
+    for (u32 w = tid; w < words; w += WG) bm[w] = 0;
+    __syncthreads();
+    for (u32 i = tid; i < cnt; i += WG) {
+        const u64 e = sm.buf[i];
+        if (e >= T) {
+            const u32 c = comp_col<E>(e);
+            atomicOr(&bm[c >> 5], 1u << (c & 31));
+        }
+    }
+    __syncthreads();
+    DSTK_PHASE(23);
+    const u32 per = (words + WG - 1) / WG;
+    const u32 w0 = tid * per;
+    u32 sum = 0;
+    for (u32 j = 0; j < per; ++j)
+        if (w0 + j < words) sum += __popc(bm[w0 + j]);
+    u32 tot;
+    sm.tbase[tid] = block_excl_scan<WG, CAP>(sm, sum, &tot);
+    __syncthreads();
+    DSTK_PHASE(24);
+    for (u32 i = tid; i < cnt; i += WG) {
+        const u64 e = sm.buf[i];
+        if (e >= T) {
+            const u32 c = comp_col<E>(e), w = c >> 5, t = w / per;
+            u32 pos = sm.tbase[t];
+            for (u32 x = t * per; x < w; ++x) pos += __popc(bm[x]);
+            pos += __popc(bm[w] & ((1u << (c & 31)) - 1u));
+            if (pos < k) {
+                out_idx[pos] = (int32_t)c;
+                if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ kernel
 struct Params {
     const uint8_t* in;
@@ -691,6 +963,83 @@ struct Slot {
     }
 };
 
+// Exact selection of the k largest of buf[0, cnt) (bin b1 holds the k-th,
+// rank r1 of c1 inside it) and output; then the NaN report.
+template <class E, int WG, int CAP>
+__device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 n, int sorted,
+                                             int retval, int flags, int32_t* row_idx, void* row_val, int32_t* flag,
+                                             int32_t flag_value) {
+    const u64 T = refine<WG, CAP>(sm, cnt, b1, r1, c1);
+    DSTK_PHASE(5);
+    emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
+    __syncthreads();
+    if (threadIdx.x == 0 && sm.nan) *flag = flag_value;
+}
+
+// Merge when the boundary bin is too large for the buffer (heavy ties
+// across segments): stream the published entries at or above the row
+// bound through the buffer, reducing to k whenever it fills.
+template <class E, int WG, int CAP>
+__device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, const u32* rdir, const u64* rc, u32 S,
+                                            u32 cap, u64 Lrow, u32 k, u32 n, int sorted, int retval, int flags,
+                                            int32_t* row_idx, void* row_val, int32_t* flag, int32_t flag_value) {
+    const u32 tid = threadIdx.x;
+    const u32 dL = top_digit(Lrow);
+    constexpr int kMI = E::kPerVec;  // entries per thread per step (one tile's worth)
+    u32 mm = 0;
+    if (tid < S) {
+        const u64 m0 = ld_agent(&rmeta[(u64)tid * 4]);
+        const u32 lv = (u32)m0, dl = (u32)(m0 >> 32);
+        const u32 dh = (u32)ld_agent(&rmeta[(u64)tid * 4 + 1]);
+        if (lv == 0 || dL > dh) mm = 0;
+        else if (dL <= dl) mm = lv;
+        else mm = ld_agent(&rdir[(u64)tid * kBins + (dh - dL)]);
+    }
+    __syncthreads();
+    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    u32 tot2;
+    const u32 off2 = block_excl_scan<WG, CAP>(sm, mm, &tot2);
+    if (tid < S) sm.seg_count[tid] = off2;
+    if (tid == 0) sm.count = 0;
+    __syncthreads();
+    for (u32 base = 0; base < tot2; base += WG * kMI) {
+        u64 e[kMI];
+        u32 pmk = 0, c = 0;
+#pragma unroll
+        for (int j = 0; j < kMI; ++j) {
+            const u32 f = base + j * WG + tid;
+            e[j] = 0;
+            if (f < tot2) {
+                u32 lo = 0, hi = S;
+                while (hi - lo > 1) {
+                    const u32 mid = (lo + hi) >> 1;
+                    if (sm.seg_count[mid] <= f) lo = mid; else hi = mid;
+                }
+                e[j] = ld_agent(&rc[(u64)lo * cap + (f - sm.seg_count[lo])]);
+            }
+            const bool ok = f < tot2 && e[j] >= Lrow;
+            pmk |= (u32)ok << j;
+            c += ok;
+        }
+        u32 pos = wave_reserve(&sm.count, c);
+        if (pos != ~0u) {
+#pragma unroll
+            for (int j = 0; j < kMI; ++j)
+                if ((pmk >> j) & 1u) {
+                    sm.buf[pos++] = e[j];
+                    atomicAdd(&sm.hist[hidx(top_digit(e[j]))], 1u);
+                }
+        }
+        __syncthreads();
+        const u32 c2 = sm.count;
+        if (c2 > (u32)(CAP - WG * kMI)) make_room<E, WG, CAP>(sm, c2, k, WG * kMI);
+    }
+    final_select<E, WG, CAP>(sm, sm.count, k);
+    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, row_idx, row_val);
+    __syncthreads();
+    if (tid == 0 && sm.nan) *flag = flag_value;
+}
+
 // One workgroup per (row, segment).  EB: element bytes; WG: threads; NV:
 // tiles per chunk (16-byte loads each thread has in flight); CAP:
 // candidate-buffer entries.
@@ -707,6 +1056,7 @@ void topk_rows(Params p) {
     static_assert(CAP >= 2 * NV * kTileElems || NV * kTileElems >= 8192, "capacity must hold two chunks");
     __shared__ Smem<CAP> sm;
 
+    DSTK_PROBE_INIT
     const u32 tid = threadIdx.x;
     const u32 row = blockIdx.x / (u32)p.segs;
     const u32 seg = blockIdx.x % (u32)p.segs;
@@ -743,6 +1093,9 @@ void topk_rows(Params p) {
         sm.L = 0;
         sm.nan = 0;
         sm.last = 0;
+        sm.outcount = 0;
+        sm.pflag[0] = 0;
+        sm.pflag[1] = 0;
     }
     DSTK_PHASE(0);
 
@@ -753,15 +1106,15 @@ void topk_rows(Params p) {
     __syncthreads();
 
     u32 pr = b;  // permuted index of the next tile to request
+    u32 par = 0;  // slot of sm.pflag used by the next overflow check
     constexpr int kSeed = NV < 2 ? NV : 2;  // tiles counted to seed the bound
     static_assert(CAP >= kSeed * kTileElems, "the seed tiles must fit an empty buffer");
 
     // Filter one tile (one vector per thread) against the bound, appending
-    // admitted elements and counting them in the histogram.  Returns false,
-    // appending nothing, when the wave's admitted elements do not fit.
-    auto filter = [&](const uint4& x, int vbi) -> bool {
-        const u32 any = pf.any(x.x) | pf.any(x.y) | pf.any(x.z) | pf.any(x.w);
-        if (__ballot(any != 0) == 0) return true;
+    // admitted elements (and counting them in the histogram when `count`).
+    // Returns false, appending nothing, when the wave's admitted elements do
+    // not fit.
+    auto filter = [&](const uint4& x, int vbi, bool count) -> bool {
         const uint4 xs[1] = {x};
         u32 pm = 0, c = 0;
 #pragma unroll
@@ -785,17 +1138,24 @@ void topk_rows(Params p) {
                     SL::get(xs, s, vbi, tid, v1, n, bits, col, valid);
                     const u64 e = compose<E>(E::key(bits), col);
                     sm.buf[pos++] = e;
-                    atomicAdd(&sm.hist[top_digit(e)], 1u);
+                    if (count) atomicAdd(&sm.hist[hidx(top_digit(e))], 1u);
                 }
             }
         }
         return true;
     };
+    // Does any element of the tile pass the float pre-filter (wave-uniform)?
+    auto maybe = [&](const uint4& x) -> bool {
+        const u32 any = pf.any(x.x) | pf.any(x.y) | pf.any(x.z) | pf.any(x.w);
+        return __ballot(any != 0) != 0;
+    };
 
-    // Phase A, per chunk of NV tiles: all NV loads requested at once and
-    // filtered in request order (straight-line code, so each tile waits only
-    // for its own load; lanes past the segment read zeros and are masked out).  After the seed, filtering
-    // takes no workgroup barrier: waves run independently and hide each
+    // Per chunk of NV tiles: all NV loads are requested at once.  A short
+    // unrolled pass waits for each tile in request order and notes which
+    // tiles have elements past the pre-filter; once the whole chunk has
+    // arrived, one rolled loop (the same code for every tile, so it is
+    // fetched once) appends their admitted elements.  After the seed no
+    // workgroup barrier is taken: waves run independently and hide each
     // other's load latency.  A wave whose entries do not fit records the
     // tile; phase B makes room and filters those tiles again.
     for (u32 t0 = 0; t0 < ntiles; t0 += NV) {
@@ -809,11 +1169,12 @@ void topk_rows(Params p) {
             pr += a;
             if (pr >= ntiles) pr -= ntiles;
         }
-        u32 pending = 0;  // wave-uniform: tiles this wave still has to append
+        u32 cand = 0;     // wave-uniform: tiles to append
+        u32 counted = 0;  // tiles already counted in the histogram (the seed)
         if (t0 == 0) {
             // Seed: count every element of the first kSeed tiles, take the
-            // bin edge of the k-th counted as the bound, then admit those
-            // tiles' elements at or above it (they always fit).
+            // bin edge of the k-th counted as the bound; those tiles are then
+            // appended (they fit an empty buffer) without counting again.
 #pragma unroll
             for (int i = 0; i < kSeed; ++i) {
                 const uint4 xs[1] = {v[i]};
@@ -824,61 +1185,58 @@ void topk_rows(Params p) {
                     SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
                     if (valid) {
                         saw_nan |= E::is_nan(bits);
-                        atomicAdd(&sm.hist[top_digit(compose<E>(E::key(bits), col))], 1u);
+                        atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(bits), col)))], 1u);
                     }
                 }
             }
+            DSTK_PHASE(19);
             __syncthreads();
-            hist_locate<WG, CAP>(sm, k);
-            if (sm.sel_c > 0) L = digit_floor(sm.sel_digit);
+            if (tid < kWave) wave_locate(sm, k, 0u, false);
+            __syncthreads();
+            if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
             pf.set(L);
-#pragma unroll
-            for (int i = 0; i < kSeed; ++i) {
-                const uint4 xs[1] = {v[i]};
-                u32 pm = 0, c = 0;
-#pragma unroll
-                for (int s = 0; s < SL::kSlots; ++s) {
-                    u32 bits, col;
-                    bool valid;
-                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
-                    const bool ok = valid && compose<E>(E::key(bits), col) >= L;
-                    pm |= (u32)ok << s;
-                    c += ok;
-                }
-                u32 pos = wave_reserve(&sm.count, c);
-                if (pos != ~0u) {
-#pragma unroll
-                    for (int s = 0; s < SL::kSlots; ++s) {
-                        if ((pm >> s) & 1u) {
-                            u32 bits, col;
-                            bool valid;
-                            SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
-                            sm.buf[pos++] = compose<E>(E::key(bits), col);
-                        }
-                    }
-                }
-            }
+            DSTK_PHASE(7);
+            cand = (1u << kSeed) - 1u;
+            counted = cand;
 #pragma unroll
             for (int i = kSeed; i < NV; ++i)
-                if (!filter(v[i], vb[i])) pending |= 1u << i;
+                if (maybe(v[i])) cand |= 1u << i;
         } else {
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                if (!filter(v[i], vb[i])) pending |= 1u << i;
+                if (maybe(v[i])) cand |= 1u << i;
+        }
+        u32 pending = 0;  // wave-uniform: tiles this wave still has to append
+#pragma unroll 1
+        for (int i = 0; i < NV; ++i) {
+            if (!((cand >> i) & 1u)) continue;
+            uint4 x = v[0];
+            int vbi = vb[0];
+#pragma unroll
+            for (int j = 1; j < NV; ++j)
+                if (i == j) {
+                    x = v[j];
+                    vbi = vb[j];
+                }
+            if (!filter(x, vbi, !((counted >> i) & 1u))) pending |= 1u << i;
         }
 
         // Phase B (rare): make room, raise the bound, filter what did not fit.
+        DSTK_PHASE(8);
         for (int round = 0; round < 64; ++round) {
+            // "any wave pending?" in one barrier: slot `par` collects the
+            // answer; the other slot, last read before an earlier barrier,
+            // is cleared for the next check
+            if (lane_id() == 0 && pending) atomicOr(&sm.pflag[par], 1u);
+            if (tid == 0) sm.pflag[par ^ 1u] = 0;
             __syncthreads();
-            if (lane_id() == 0 && pending) atomicOr(&sm.last, 1u);
-            __syncthreads();
-            const bool again = sm.last != 0;
-            __syncthreads();
+            const bool again = sm.pflag[par] != 0;
+            par ^= 1u;
             if (!again) break;
-            if (tid == 0) sm.last = 0;
             make_room<E, WG, CAP>(sm, sm.count, k, kTileElems);
-            hist_locate<WG, CAP>(sm, k);
-            if (sm.sel_c > 0 && digit_floor(sm.sel_digit) > L) L = digit_floor(sm.sel_digit);
+            if (tid < kWave) wave_locate(sm, k, 0u, false);
+            __syncthreads();
+            if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
             const u32 todo = pending;
@@ -886,15 +1244,16 @@ void topk_rows(Params p) {
             for (int i = 0; i < NV; ++i) {
                 if ((todo >> i) & 1u) {
                     const uint4 x = load_vec(vb[i] + (int)tid);  // cached: read moments ago
-                    if (!filter(x, vb[i])) pending |= 1u << i;
+                    if (!filter(x, vb[i], !((counted >> i) & 1u))) pending |= 1u << i;
                 }
             }
         }
         // Between chunks (long segments only): tidy up and raise the bound.
         if (t0 + NV < ntiles) {
             if (sm.count > (u32)CAP / 2) make_room<E, WG, CAP>(sm, sm.count, k, 0);
-            hist_locate<WG, CAP>(sm, k);
-            if (sm.sel_c > 0 && digit_floor(sm.sel_digit) > L) L = digit_floor(sm.sel_digit);
+            if (tid < kWave) wave_locate(sm, k, 0u, false);
+            __syncthreads();
+            if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
         }
@@ -903,202 +1262,215 @@ void topk_rows(Params p) {
     if (tid == 0) sm.L = L;
     DSTK_PHASE(1);
     __syncthreads();
+    DSTK_PHASE(9);
     u32 cnt = sm.count;
+    const u32 wave = tid / kWave;
+    int32_t* const row_idx = p.out_idx + (int64_t)row * k;
+    void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr;
 
     if (p.segs == 1) {
-        final_select<E, WG, CAP>(sm, cnt, k);
-        DSTK_PHASE(2);
-        emit<E, WG, CAP>(sm, k, n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
-                         p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
+        if (wave == 0) wave_locate(sm, k, 0u, true);
         __syncthreads();
-        if (tid == 0 && sm.nan) *p.flag = p.flag_value;
+        DSTK_PHASE(2);
+        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, n, p.sorted, p.retval,
+                                    p.flags, row_idx, row_val, p.flag, p.flag_value);
         DSTK_PHASE(6);
+        DSTK_PROBE_FLUSH();
         return;
     }
 
-    // ---- split row: publish this segment's live candidates, sorted by top
-    // digit, with a directory of cumulative counts per digit.
+    // ---- split row: publish this segment's live candidates (entries in the
+    // bin of its k-th counted entry or above) in descending top-digit order,
+    // with a directory dir[j] = number of entries with top digit >= d_hi - j.
     const u32 S = (u32)p.segs;
     const u32 slot = row * S + seg;
     {
-        // bound for rank q = ceil(k / S): with every segment's list holding
-        // q entries at or above its own such bound, the smallest of them is
-        // a valid bound for the row
+        // q = ceil(k / S): with every segment holding q entries at or above
+        // its q-bound, the smallest q-bound over the row is a valid bound too
         const u32 q = (k + S - 1) / S;
-        hist_locate<WG, CAP>(sm, q);
-        const u64 bq = sm.sel_c > 0 ? digit_floor(sm.sel_digit) : 0ull;
-        hist_locate<WG, CAP>(sm, k);
-        u32 dl = sm.sel_c > 0 ? sm.sel_digit : 0u;
-        u32 live = sm.sel_c > 0 ? sm.sel_above + sm.sel_c : sm.sel_total;
+        if (wave == 0) wave_locate(sm, k, q, false);
+        DSTK_PHASE(11);
+        __syncthreads();
+        u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
+        u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
+        u64 bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
         if (live > (u32)p.pub_cap) {
             // too many to publish: reduce this segment exactly to k first
-            compact_to_k<E, WG, CAP>(sm, cnt, k);
-            rebuild_hist<WG, CAP>(sm, k);
-            cnt = k;
-            hist_locate<WG, CAP>(sm, k);
-            dl = sm.sel_digit;
-            live = sm.sel_above + sm.sel_c;
-            if (L < sm.L) L = sm.L;
+            cnt = reduce_to_k<WG, CAP>(sm, cnt, k, q, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0]);
+            if (sm.kth > L) L = sm.kth;
+            dl = sm.loc_digit[0];
+            live = sm.loc_above[0] + sm.loc_c[0];
+            bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
         }
-        // hist[d] -> number of live entries in higher bins (for d >= dl);
-        // directory: entries with digit >= d, written for d in [dl, d_hi]
-        constexpr int kPer = kBins / WG;
-        u32 hv[kPer];
-        u32 sum = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const u32 d = kBins - 1 - tid * kPer - j;
-            hv[j] = d >= dl ? sm.hist[d] : 0u;
-            sum += hv[j];
-        }
-        u32 tot;
-        u32 run = block_excl_scan<WG, CAP>(sm, sum, &tot);
+        DSTK_PHASE(10);
+        const u32 dh = sm.loc_dhi;
         u32* dir = p.ws_dir + (u64)slot * kBins;
-        if (run == 0 && sum > 0) {
-#pragma unroll
-            for (int j = kPer - 1; j >= 0; --j)
-                if (hv[j]) sm.d_hi = kBins - 1 - tid * kPer - j;
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const u32 d = kBins - 1 - tid * kPer - j;
-            if (d >= dl) {
-                sm.hist[d] = run;
-                run += hv[j];
-                if (run > 0) dir[d - dl] = run;
+        if (wave == 0) {
+            // placement offsets (entries in higher bins) for bins in [dl, dh],
+            // written over the histogram, and the directory; 64 bins a step,
+            // lane i taking bin dh - step - i (descending)
+            const u32 l = lane_id();
+            if (live > 0) {
+                u32 carry = 0;
+                for (u32 b0 = 0; b0 <= dh - dl; b0 += kWave) {
+                    const u32 j = b0 + l;
+                    const bool in = j <= dh - dl;
+                    const u32 c = in ? sm.hist[hidx(dh - j)] : 0u;
+                    const u32 ci = wave_incl_scan(c);
+                    if (in) {
+                        sm.hist[hidx(dh - j)] = carry + ci - c;
+                        st_agent(&dir[j], carry + ci);
+                    }
+                    carry += __builtin_amdgcn_readlane(ci, 63);
+                }
+            }
+            if (l == 0) {
+                u64* meta = p.ws_meta + (u64)slot * 4;
+                st_agent(&meta[0], (u64)live | ((u64)dl << 32));
+                st_agent(&meta[1], (u64)(live ? dh : 0u));
+                st_agent(&meta[2], L);
+                st_agent(&meta[3], bq);
             }
         }
         __syncthreads();
         u64* cand = p.ws_cand + (u64)slot * (u32)p.pub_cap;
-        constexpr int kItems = CAP / WG;
-        u64 mine[kItems];
-        u32 at[kItems];
-#pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const u32 i = tid + j * WG;
-            mine[j] = i < cnt ? sm.buf[i] : 0ull;
-            at[j] = (i < cnt && top_digit(mine[j]) >= dl) ? atomicAdd(&sm.hist[top_digit(mine[j])], 1u) : ~0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kItems; ++j)
-            if (at[j] != ~0u) cand[at[j]] = mine[j];
-        if (tid == 0) {
-            u64* meta = p.ws_meta + (u64)slot * 4;
-            meta[0] = (u64)live | ((u64)dl << 32);
-            meta[1] = (u64)(live ? sm.d_hi : 0u);
-            meta[2] = L;
-            meta[3] = bq;
+        for (u32 i = tid; i < cnt; i += WG) {
+            const u64 e = sm.buf[i];
+            const u32 d = top_digit(e);
+            if (live > 0 && d >= dl) {
+                const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
+                if (pos < (u32)p.pub_cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
+            }
         }
     }
     DSTK_PHASE(2);
+    // Hand-off: this wave's device-coherent stores have completed; once every
+    // wave is past the barrier, one relaxed ticket increment publishes the
+    // segment.  The last of the row's segments merges.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    DSTK_PHASE(12);
     if (tid == 0) {
-        // release this workgroup's stores (ordered before by the barrier) to
-        // the device, then take a ticket; the last ticket merges
-        __threadfence();
-        const u32 prev = atomicAdd(&p.ws_ticket[row], 1u);
+        const u32 prev = __hip_atomic_fetch_add(&p.ws_ticket[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm.last = prev == S - 1;
-        if (sm.last) __threadfence();
     }
     __syncthreads();
     if (!sm.last) {
         if (tid == 0 && sm.nan) *p.flag = p.flag_value;
         DSTK_PHASE(3);
+        DSTK_PROBE_FLUSH();
         return;
     }
     DSTK_PHASE(4);
 
-    // Merge.  Every element of the row's top-k is among some segment's live
-    // list.  Bounds: a segment with at least k elements has k of them at or
-    // above its bound; every segment has q = ceil(k/S) at or above its
-    // q-bound, so the smallest q-bound over the row is valid as well.
+    // ---- merge.  Every element of the row's top-k is in some segment's
+    // published list.  Row bound: the largest segment bound, or the smallest
+    // q-bound if that is larger; only digits at or above it are counted.
     const u32 cap = (u32)p.pub_cap;
     const u64* rc = p.ws_cand + (u64)row * S * cap;
+    const u32* rdir = p.ws_dir + (u64)row * S * kBins;
+    constexpr u32 kDirCache = 32;  // directory entries read with the metadata
+    u64* mc = sm.buf;                                 // [S][4] metadata
+    u32* dc = (u32*)(sm.buf + 4 * S);                 // [S][kDirCache] directory heads
+    for (u32 i = tid; i < S * 4; i += WG) mc[i] = ld_agent(&p.ws_meta[(u64)row * S * 4 + i]);
+    for (u32 i = tid; i < S * kDirCache; i += WG)
+        dc[i] = ld_agent(&rdir[(u64)(i / kDirCache) * kBins + (i % kDirCache)]);
     for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    if (tid == 0) p.ws_ticket[row] = 0;  // ready for the next call
+    __syncthreads();
+    DSTK_PHASE(15);
+    auto dirv = [&](u32 s_, u32 j) -> u32 {  // entries of segment s_ with digit >= d_hi - j
+        return j < kDirCache ? dc[s_ * kDirCache + j] : ld_agent(&rdir[(u64)s_ * kBins + j]);
+    };
+    u64 Lrow;
     {
-        u64 m0 = 0, m1 = 0, m2 = 0, m3 = ~0ull;
-        if (tid < S) {
-            const u64* meta = p.ws_meta + (u64)(row * S + tid) * 4;
-            m0 = meta[0];
-            m1 = meta[1];
-            m2 = meta[2];
-            m3 = meta[3];
+        u64 lmax = 0, qmin = ~0ull;
+        for (u32 s_ = tid; s_ < S; s_ += WG) {
+            lmax = mc[s_ * 4 + 2] > lmax ? mc[s_ * 4 + 2] : lmax;
+            qmin = mc[s_ * 4 + 3] < qmin ? mc[s_ * 4 + 3] : qmin;
         }
-        // row bound: max over segment bounds, max with min over q-bounds
-        u64 vmax = wave_max64(m2), vmin = wave_min64(m3);
-        const u32 wave = tid / kWave;
+        lmax = wave_max64(lmax);
+        qmin = wave_min64(qmin);
         if (lane_id() == 0) {
-            sm.red[wave][0] = vmax;
-            sm.red[wave][1] = vmin;
+            sm.red[wave][0] = lmax;
+            sm.red[wave][1] = qmin;
         }
         __syncthreads();
-        u64 lmax = 0, qmin = ~0ull;
+        lmax = 0;
+        qmin = ~0ull;
 #pragma unroll
         for (u32 w = 0; w < WG / kWave; ++w) {
             lmax = sm.red[w][0] > lmax ? sm.red[w][0] : lmax;
             qmin = sm.red[w][1] < qmin ? sm.red[w][1] : qmin;
         }
-        L = lmax > qmin ? lmax : qmin;
-        const u32 df = top_digit(L);
-        u32 m = 0;
-        if (tid < S) {
-            const u32 live = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)m1;
-            if (live == 0 || df > dh) m = 0;
-            else if (df <= dl) m = live;
-            else m = p.ws_dir[(u64)(row * S + tid) * kBins + (df - dl)];
-        }
-        u32 total;
-        const u32 off = block_excl_scan<WG, CAP>(sm, m, &total);
-        if (tid < S) sm.seg_count[tid] = off;
-        if (tid == 0) {
-            sm.newtotal = total;
-            sm.count = 0;
-            p.ws_ticket[row] = 0;  // ready for the next call
-        }
-        __syncthreads();
+        Lrow = lmax > qmin ? lmax : qmin;
     }
-    const u32 total = sm.newtotal;
-    constexpr int kMI = kTileElems / WG;  // merge entries per thread per step
-    for (u32 base = 0; base < total; base += WG * kMI) {
-        u64 e[kMI];
-        u32 pm = 0, c = 0;
-#pragma unroll
-        for (int j = 0; j < kMI; ++j) {
-            const u32 f = base + j * WG + tid;
-            e[j] = 0;
-            if (f < total) {
-                u32 lo = 0, hi = S;  // last segment whose offset is <= f
-                while (hi - lo > 1) {
-                    const u32 mid = (lo + hi) >> 1;
-                    if (sm.seg_count[mid] <= f) lo = mid; else hi = mid;
-                }
-                e[j] = rc[(u64)lo * cap + (f - sm.seg_count[lo])];
-            }
-            const bool ok = f < total && e[j] >= L;
-            pm |= (u32)ok << j;
-            c += ok;
+    DSTK_PHASE(16);
+    const u32 dL = top_digit(Lrow);
+    // row histogram of the published entries with digit >= dL, from the directories
+    for (u32 s_ = wave; s_ < S; s_ += WG / kWave) {
+        const u64 m0 = mc[s_ * 4];
+        const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+        if (lv == 0 || dh < dL) continue;
+        const u32 np = dh - (dl > dL ? dl : dL) + 1;
+        for (u32 j = lane_id(); j < np; j += kWave) {
+            const u32 c = dirv(s_, j) - (j ? dirv(s_, j - 1) : 0u);
+            if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
         }
-        u32 pos = wave_reserve(&sm.count, c);
-        if (pos != ~0u) {
-#pragma unroll
-            for (int j = 0; j < kMI; ++j)
-                if ((pm >> j) & 1u) {
-                    sm.buf[pos++] = e[j];
-                    atomicAdd(&sm.hist[top_digit(e[j])], 1u);
-                }
-        }
-        __syncthreads();
-        const u32 c2 = sm.count;
-        if (c2 > (u32)(CAP - kTileElems)) make_room<E, WG, CAP>(sm, c2, k, kTileElems);
     }
-    cnt = sm.count;
-    final_select<E, WG, CAP>(sm, cnt, k);
-    DSTK_PHASE(5);
-    emit<E, WG, CAP>(sm, k, n, p.sorted, p.retval, p.flags, p.out_idx + (int64_t)row * k,
-                     p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr);
     __syncthreads();
-    if (tid == 0 && sm.nan) *p.flag = p.flag_value;
+    DSTK_PHASE(17);
+    if (wave == 0) wave_locate(sm, k, 0u, true);
+    __syncthreads();
+    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0];
+    DSTK_PHASE(18);
+    // entries each segment contributes: those with digit >= b1, a prefix of its list
+    u32 m = 0;
+    if (tid < S) {
+        const u64 m0 = mc[tid * 4];
+        const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[tid * 4 + 1];
+        if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(tid, dh - b1);
+    }
+    u32 total;
+    const u32 off = block_excl_scan<WG, CAP>(sm, m, &total);
+    if (tid < S) sm.seg_count[tid] = off;
+    __syncthreads();
+    DSTK_PHASE(13);
+    if (total > (u32)CAP) {
+        merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, Lrow, k, n, p.sorted, p.retval,
+                                   p.flags, row_idx, row_val, p.flag, p.flag_value);
+        return;
+    }
+    {
+        constexpr int kLB = 4;  // loads in flight per thread
+        for (u32 base = 0; base < total; base += WG * kLB) {
+            u64 v[kLB];
+#pragma unroll
+            for (int u = 0; u < kLB; ++u) {
+                const u32 f = base + u * WG + tid;
+                v[u] = 0;
+                if (f < total) {
+                    u32 lo = 0, hi = S;  // last segment whose offset is <= f
+                    while (hi - lo > 1) {
+                        const u32 mid = (lo + hi) >> 1;
+                        if (sm.seg_count[mid] <= f) lo = mid; else hi = mid;
+                    }
+                    v[u] = ld_agent(&rc[(u64)lo * cap + (f - sm.seg_count[lo])]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kLB; ++u) {
+                const u32 f = base + u * WG + tid;
+                if (f < total) sm.buf[f] = v[u];
+            }
+        }
+    }
+    __syncthreads();
+    DSTK_PHASE(14);
+    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, n, p.sorted, p.retval, p.flags, row_idx, row_val, p.flag,
+                                p.flag_value);
     DSTK_PHASE(6);
+    DSTK_PROBE_FLUSH();
 }
 
 }  // namespace dstk

@@ -186,3 +186,22 @@ def test_repeatability(pkg, cfg):
         _, uidx = pkg.topk(x, w.k, sorted_index=False, return_value=False, n=w.n)
         assert np.array_equal(np.sort(uidx.cpu().numpy(), axis=1), ref)
     pkg.ds_topk_set_overrides(0, 0)
+
+
+def test_repeated_calls_overflow_path(pkg, oracle_mod):
+    """The full ragged-decode workload (rows whose -inf tails fill whole
+    segments, so candidate buffers overflow and tiles are filtered again),
+    called back to back: every call returns DS_OK and the oracle's sets."""
+    from workloads import make_workload
+
+    w = make_workload("C4")
+    st, oidx, _ = oracle_mod.topk(w.raw, w.dtype, w.n, w.k, False, False, nthreads=0)
+    assert st == 0
+    want = np.sort(oidx, axis=1)
+    x = to_device(w.raw, w.dtype)
+    log("repeated C4 calls")
+    for rep in range(20):
+        val, idx = pkg.topk(x, w.k, sorted_index=False, return_value=True, n=w.n)
+        got = np.sort(idx.cpu().numpy(), axis=1)
+        bad = np.nonzero(np.any(got != want, axis=1))[0]
+        assert bad.size == 0, "call %d: rows %s differ" % (rep, bad[:8].tolist())
