@@ -29,7 +29,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -44,23 +43,11 @@ METRIC = "effective HBM GB/s (% peak), bf16 4×204800 k=1024 & fp32 64×129280 k
 PEAK_GBS = 8000.0  # MI355X HBM3E
 STEP_WORKLOADS = ("C2", "C3")
 DOMINANT = "C3"
-KERNEL_SOURCES = ("sampling_topk_selection_amd/csrc/topk_kernels.hpp",
-                  "sampling_topk_selection_amd/csrc/ds_topk.hip",
-                  "sampling_topk_selection_amd/build.py")
-
-
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
+TRAFFIC_FILES = {"C3": "topk_rows_fp32_sampler_64x129280_k512_traffic.txt"}
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES[workload])
     if not os.path.exists(path):
         return None
     kv = {}
@@ -68,6 +55,8 @@ def load_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
+    from sampling_topk_selection_amd.build import kernel_source_sha
+
     if kv.get("kernel_source_sha") != kernel_source_sha():
         return None
     try:
@@ -143,7 +132,7 @@ def main() -> int:
         W[cfg] = dict(w=w, X=X, copies=copies, dt=dt, idx=idx, val=val, plan=plan,
                       bytes=w.algorithmic_bytes(), x0=x0)
 
-    nstatus = args.warmup + args.steps + 4 * args.steps + 16
+    nstatus = args.warmup + 2 * args.steps + 4 * max(20, args.steps) + 64
     status = torch.zeros(nstatus, dtype=torch.int32, device=dev)
     slot = [0]
 
@@ -254,24 +243,42 @@ def main() -> int:
             calib.calib_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(), 2048, sptr)
         torch.cuda.synchronize()
 
+    # the dominant kernel alone, launched back to back: average launch
+    # duration over the timed region (events on the stream it runs on)
+    dom_reps = max(20, args.steps)
+    for i in range(3):
+        call(DOMINANT, i)
+    a_ev = torch.cuda.Event(enable_timing=True)
+    b_ev = torch.cuda.Event(enable_timing=True)
+    a_ev.record(stream)
+    for i in range(dom_reps):
+        call(DOMINANT, i)
+    b_ev.record(stream)
+    torch.cuda.synchronize()
+    dom_us = a_ev.elapsed_time(b_ev) * 1e3 / dom_reps
+
     torch.cuda.synchronize()
     st = status.cpu().numpy()
     if np.any(st != 0):
         raise RuntimeError("a timed call reported status %s" % np.unique(st).tolist())
 
     # ---------------------------------------------------------------- roofline (dominant kernel)
-    dom = per.get(DOMINANT)
-    achieved = dom["GBps"] if dom else None
+    from sampling_topk_selection_amd.build import kernel_source_sha
+
+    achieved = W[DOMINANT]["bytes"] / (dom_us * 1e-6) / 1e9
     traffic = load_traffic(DOMINANT)
     roofline = {
         "bound": "hbm",
-        "kernel": "topk_rows (fp32 sampler shape, %s)" % W[DOMINANT]["w"].dtype,
-        "achieved": achieved,
+        "kernel": "topk_rows<4, 512, %d, %d> (fp32 sampler shape: 64 x 129280, k=512)" % (
+            W[DOMINANT]["plan"].tiles_per_chunk, W[DOMINANT]["plan"].capacity),
+        "achieved": round(achieved, 1),
         "peak": PEAK_GBS,
         "unit": "GB/s",
-        "frac": round(achieved / PEAK_GBS, 4) if achieved else None,
+        "frac": round(achieved / PEAK_GBS, 4),
         "traffic": traffic,
         "algorithmic_bytes_per_launch": W[DOMINANT]["bytes"],
+        "avg_launch_us": round(dom_us, 3),
+        "launches_timed": dom_reps,
         "kernel_source_sha": kernel_source_sha(),
     }
 

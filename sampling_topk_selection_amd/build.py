@@ -5,6 +5,7 @@
 
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -18,6 +19,20 @@ CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
 CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Files whose content decides the top-k kernels' code (for tagging profiles).
+KERNEL_SOURCES = (SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(ROOT, "include", "ds_topk.h"),
+                  os.path.abspath(__file__))
+
+
+def kernel_source_sha() -> str:
+    """Short hash of the kernel sources and build flags: a counter summary
+    taken on other sources no longer describes the kernel."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 FLAGS = [
     "--offload-arch=gfx950",
