@@ -19,7 +19,7 @@ namespace {
 
 constexpr int kVersion = 100;       // 0.1.0
 constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS count each)
-constexpr int kTargetWG = 512;      // about two workgroups per CU on a 256-CU MI355X
+constexpr int kTargetWG = 256;      // one workgroup per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
 #ifndef DS_TOPK_TILES_PER_CHUNK
 #define DS_TOPK_TILES_PER_CHUNK 4

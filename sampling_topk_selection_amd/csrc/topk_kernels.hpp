@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dstk {
 
 using u32 = uint32_t;
@@ -102,6 +104,10 @@ struct PreFilter<Elem<2>> {
     __device__ u32 any(u32 d) const {
         return (u32)!(__uint_as_float(d) < t_hi) | (u32)!(__uint_as_float(d << 16) < t_lo);
     }
+    // bit 0: the low half may pass, bit 1: the high half may pass
+    __device__ u32 pass2(u32 d) const {
+        return (u32)!(__uint_as_float(d << 16) < t_lo) | ((u32)!(__uint_as_float(d) < t_hi) << 1);
+    }
 };
 
 template <>
@@ -111,21 +117,44 @@ struct PreFilter<Elem<4>> {
     __device__ u32 any(u32 d) const { return (u32)!(__uint_as_float(d) < t); }
 };
 
+// Per-slot pre-filter mask of one 16-byte vector (bit s: element s may be at
+// or above the bound; NaN always passes).  Slot order is element order.
+__device__ __forceinline__ u32 pass_mask(const PreFilter<Elem<4>>& pf, const uint4& x) {
+    return pf.any(x.x) | (pf.any(x.y) << 1) | (pf.any(x.z) << 2) | (pf.any(x.w) << 3);
+}
+__device__ __forceinline__ u32 pass_mask(const PreFilter<Elem<2>>& pf, const uint4& x) {
+    return pf.pass2(x.x) | (pf.pass2(x.y) << 2) | (pf.pass2(x.z) << 4) | (pf.pass2(x.w) << 6);
+}
+// Raw bits of element s of a 16-byte vector given as its four words (by
+// value: selecting among registers, never indexing memory).
+__device__ __forceinline__ u32 slot_bits(Elem<4>, u32 x0, u32 x1, u32 x2, u32 x3, u32 s) {
+    const u32 lo = (s & 1u) ? x1 : x0, hi = (s & 1u) ? x3 : x2;
+    return (s & 2u) ? hi : lo;
+}
+__device__ __forceinline__ u32 slot_bits(Elem<2>, u32 x0, u32 x1, u32 x2, u32 x3, u32 s) {
+    const u32 lo = (s & 2u) ? x1 : x0, hi = (s & 2u) ? x3 : x2;
+    const u32 d = (s & 4u) ? hi : lo;
+    return (d >> ((s & 1u) * 16u)) & 0xFFFFu;
+}
+
 // ------------------------------------------------------------------ shared
 constexpr int kHistBits = 11;  // radix-select digit width
 constexpr int kBins = 1 << kHistBits;
 constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
 
-// Histogram storage is transposed: bin d lives at ((d mod 32) * 64 + d / 32),
-// so the 32 consecutive bins one lane owns in wave_locate form a column that
-// it reads with immediate offsets from one address, and a row of 64 lanes
-// hits 64 consecutive words (no bank conflicts).
-__device__ __forceinline__ u32 hidx(u32 d) { return ((d & 31u) << 6) | (d >> 5); }
+// Histogram storage is transposed with a padded row: bin d lives at
+// ((d mod 32) * 65 + d / 32).  The 32 consecutive bins one lane owns in
+// wave_locate form a column that it reads with immediate offsets from one
+// address; a row read by 64 lanes, and atomics on consecutive bins (the hot
+// bins next to the bound), hit distinct banks.
+constexpr int kHistRow = 65;
+constexpr int kHistWords = 32 * kHistRow;
+__device__ __forceinline__ u32 hidx(u32 d) { return (d & 31u) * (u32)kHistRow + (d >> 5); }
 
 template <int CAP>
 struct Smem {
     u64 buf[CAP];      // candidate composites
-    u32 hist[kBins];   // radix-select histogram
+    u32 hist[kHistWords];  // radix-select histogram (bin d at hidx(d))
     u64 red[16][3];    // per-wave OR / AND / MIN
     u64 L;             // admission bound: admit iff composite >= L
     u64 kth;           // k-th composite after the last compaction
@@ -142,6 +171,7 @@ struct Smem {
     u32 loc_total, loc_dhi;
     u32 outcount;        // emit: output slots handed out
     u32 pflag[2];        // scan: "some wave has a tile left over", two slots
+    u64 stage[8][256];   // scan: per-wave staging of pre-filter survivors (raw bits << 32 | column)
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
 #ifdef DSTK_PROBE_SLOTS
     u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
@@ -234,13 +264,12 @@ __device__ __forceinline__ u32 wave_reserve(u32* counter, u32 c) {
     return base + incl - c;
 }
 
-// As wave_reserve, but never past `cap`: returns kFull (and reserves
-// nothing) when the wave's entries do not fit.  Lock-free CAS by one lane.
+// Reserve `tot` consecutive slots for the wave behind *counter, never past
+// `cap`.  Returns the first slot, or kFull (reserving nothing) when they do
+// not fit.  The result is wave-uniform (read from lane 0), so branches on it
+// stay uniform.  Lock-free CAS by one lane.
 constexpr u32 kFull = 0xFFFFFFFEu;
-__device__ __forceinline__ u32 wave_reserve_cap(u32* counter, u32 c, u32 cap) {
-    const u32 incl = wave_incl_scan(c);
-    const u32 tot = __builtin_amdgcn_readlane(incl, 63);
-    if (tot == 0) return ~0u;
+__device__ __forceinline__ u32 wave_reserve_base(u32* counter, u32 tot, u32 cap) {
     u32 base = 0;
     if (lane_id() == 0) {
         u32 old = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -257,8 +286,7 @@ __device__ __forceinline__ u32 wave_reserve_cap(u32* counter, u32 c, u32 cap) {
             old = seen;
         }
     }
-    base = __builtin_amdgcn_readfirstlane(base);
-    return base == kFull ? kFull : base + incl - c;
+    return __builtin_amdgcn_readfirstlane(base);
 }
 
 // ------------------------------------------------------------------ block helpers
@@ -289,7 +317,7 @@ constexpr int kBatch = 8;  // LDS loads kept in flight per thread in buffer pass
 template <int WG, int CAP>
 __device__ __forceinline__ void block_minmax(Smem<CAP>& sm, u32 lo, u32 hi, u64 prefix, u64 mask, u64& mn, u64& mx) {
     const u32 tid = threadIdx.x;
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     u64 vmn = ~0ull, vmx = 0;
     for (u32 base = lo; base < hi; base += WG * kBatch) {
         u64 v[kBatch];
@@ -520,7 +548,7 @@ __device__ __forceinline__ u64 digit_floor(u32 d) { return (u64)d << (64 - kHist
 template <int WG, int CAP>
 __device__ __forceinline__ void rebuild_hist(Smem<CAP>& sm, u32 cnt) {
     const u32 tid = threadIdx.x;
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     __syncthreads();
     for (u32 i = tid; i < cnt; i += WG) atomicAdd(&sm.hist[hidx(top_digit(sm.buf[i]))], 1u);
     __syncthreads();
@@ -681,10 +709,10 @@ __device__ __forceinline__ u64 low_mask(int b) { return b >= 64 ? ~0ull : ((1ull
 template <int CAP>
 __device__ __noinline__ void wave_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero) {
     const u32 l = lane_id();
-    u32* hc = sm.hist + (63u - l);  // this lane's bins, kBins - 32 (l + 1) + j, at hc[64 j]
+    u32* hc = sm.hist + (63u - l);  // this lane's bins, kBins - 32 (l + 1) + j, at hc[kHistRow j]
     u32 s = 0;
 #pragma unroll
-    for (u32 j = 0; j < 32; ++j) s += hc[64 * j];
+    for (u32 j = 0; j < 32; ++j) s += hc[kHistRow * j];
     const u32 incl = wave_incl_scan(s);
     const u32 excl = incl - s;
     if (l == 63) sm.loc_total = incl;
@@ -731,7 +759,7 @@ __device__ __noinline__ void wave_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zer
     }
     if (zero) {
 #pragma unroll
-        for (u32 j = 0; j < 32; ++j) hc[64 * j] = 0;
+        for (u32 j = 0; j < 32; ++j) hc[kHistRow * j] = 0;
     }
 }
 
@@ -817,7 +845,7 @@ template <int WG, int CAP>
 __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u32 b1, u32 r1, u32 c1) {
     const u32 tid = threadIdx.x;
     __syncthreads();
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     __syncthreads();
     const u64 T = refine<WG, CAP>(sm, cnt, b1, r1, c1);
     __syncthreads();
@@ -996,7 +1024,7 @@ __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, con
         else mm = ld_agent(&rdir[(u64)tid * kBins + (dh - dL)]);
     }
     __syncthreads();
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     u32 tot2;
     const u32 off2 = block_excl_scan<WG, CAP>(sm, mm, &tot2);
     if (tid < S) sm.seg_count[tid] = off2;
@@ -1046,7 +1074,7 @@ __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, con
 // A "tile" is one vector per thread, WG * 16 bytes; tiles are visited in a
 // pseudo-random order, a chunk at a time.
 template <int EB, int WG, int NV, int CAP>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu((CAP <= 8192 ? 2 : 1) * WG / 256)))
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WG / 256)))
 void topk_rows(Params p) {
     using E = Elem<EB>;
     using SL = Slot<E, 1, WG>;
@@ -1087,7 +1115,7 @@ void topk_rows(Params p) {
         b = h % ntiles;
     }
 
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     if (tid == 0) {
         sm.count = 0;
         sm.L = 0;
@@ -1110,57 +1138,92 @@ void topk_rows(Params p) {
     constexpr int kSeed = NV < 2 ? NV : 2;  // tiles counted to seed the bound
     static_assert(CAP >= kSeed * kTileElems, "the seed tiles must fit an empty buffer");
 
-    // Filter one tile (one vector per thread) against the bound, appending
-    // admitted elements (and counting them in the histogram when `count`).
-    // Returns false, appending nothing, when the wave's admitted elements do
-    // not fit.
-    auto filter = [&](const uint4& x, int vbi, bool count) -> bool {
-        const uint4 xs[1] = {x};
-        u32 pm = 0, c = 0;
-#pragma unroll
-        for (int s = 0; s < SL::kSlots; ++s) {
-            u32 bits, col;
-            bool valid;
-            SL::get(xs, s, vbi, tid, v1, n, bits, col, valid);
-            saw_nan |= valid && E::is_nan(bits);
-            const bool ok = valid && compose<E>(E::key(bits), col) >= L;
-            pm |= (u32)ok << s;
-            c += ok;
-        }
-        u32 pos = wave_reserve_cap(&sm.count, c, (u32)CAP);
-        if (pos == kFull) return false;
-        if (pos != ~0u) {
-#pragma unroll
-            for (int s = 0; s < SL::kSlots; ++s) {
-                if ((pm >> s) & 1u) {
-                    u32 bits, col;
-                    bool valid;
-                    SL::get(xs, s, vbi, tid, v1, n, bits, col, valid);
-                    const u64 e = compose<E>(E::key(bits), col);
-                    sm.buf[pos++] = e;
-                    if (count) atomicAdd(&sm.hist[hidx(top_digit(e))], 1u);
-                }
+    // Each wave stages the elements that pass the float pre-filter (raw
+    // bits and column) in its own LDS area, then flushes them 64 at a time
+    // with full lanes: decode, exact composite test against L, append and
+    // count.  The work per tile then follows the admissions, not the tile
+    // size, and ties with the bound's value (long runs of equal values) are
+    // filtered densely.
+    constexpr u32 kStageCap = 256;
+    static_assert(sizeof(sm.stage[0]) / sizeof(u64) == kStageCap && WG / kWave <= 8, "stage layout");
+    u64* const stage = sm.stage[tid / kWave];
+    u32 sbeg = 0, send = 0;  // wave-uniform: this wave's staged window
+    // Returns false, leaving the unflushed batch staged, when it does not fit.
+    auto flush = [&]() __attribute__((always_inline)) -> bool {
+        for (; sbeg < send; sbeg += kWave) {
+            const u32 i = sbeg + lane_id();
+            const bool in = i < send;
+            const u64 st = in ? stage[i] : 0ull;
+            const u32 bits = (u32)(st >> 32);
+            saw_nan |= in && E::is_nan(bits);
+            const u64 e = compose<E>(E::key(bits), (u32)st);
+            const bool ok = in && e >= L;
+            const u64 m = __ballot(ok);
+            if (m == 0) continue;
+            const u32 base = wave_reserve_base(&sm.count, (u32)__popcll(m), (u32)CAP);
+            if (base == kFull) return false;  // uniform: the batch stays staged
+            if (ok) {
+                sm.buf[base + mbcnt(m)] = e;
+                atomicAdd(&sm.hist[hidx(top_digit(e))], 1u);
             }
         }
+        sbeg = send = 0;
+        return true;
+    };
+    // Stage the pre-filter survivors of group g (slots 4g .. 4g+3) of one
+    // tile: each lane writes its survivors behind a wave prefix sum, in
+    // straight-line code.  Returns false when the stage cannot take them
+    // and cannot be flushed.
+    constexpr u32 kGroups = (u32)E::kPerVec / 4u;
+    auto stage_group = [&](const uint4 x, int vbi, u32 g) __attribute__((always_inline)) -> bool {
+        const u32 x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
+        const int vi = vbi + (int)tid;
+        u32 pm = (pass_mask(pf, x) >> (4u * g)) & 0xFu;
+        if (!(vbi + kTileVecs <= v1 && (u32)(vbi + kTileVecs) * E::kPerVec <= n)) {
+            // the tile runs past the valid columns: mask the invalid slots
+            u32 vm = 0;
+#pragma unroll
+            for (u32 q = 0; q < 4u; ++q)
+                vm |= (u32)(vi < v1 && (u32)vi * E::kPerVec + 4u * g + q < n) << q;
+            pm &= vm;
+        }
+        // one ballot per slot: slot q's survivors go behind those of the
+        // slots before it (independent, short dependency chains)
+        u64 b[4];
+        u32 o[4];
+        u32 tot = 0;
+#pragma unroll
+        for (u32 q = 0; q < 4u; ++q) {
+            b[q] = __ballot((pm >> q) & 1u);
+            o[q] = tot;
+            tot += (u32)__popcll(b[q]);
+        }
+        if (tot == 0) return true;
+        if (send + tot > kStageCap && !flush()) return false;
+        const u32 col0 = (u32)vi * E::kPerVec + 4u * g;
+#pragma unroll
+        for (u32 q = 0; q < 4u; ++q)
+            if ((pm >> q) & 1u)
+                stage[send + o[q] + mbcnt(b[q])] = ((u64)slot_bits(E{}, x0, x1, x2, x3, 4u * g + q) << 32) | (col0 + q);
+        send += tot;
         return true;
     };
     // Does any element of the tile pass the float pre-filter (wave-uniform)?
-    auto maybe = [&](const uint4& x) -> bool {
+    auto maybe = [&](const uint4& x) __attribute__((always_inline)) -> bool {
         const u32 any = pf.any(x.x) | pf.any(x.y) | pf.any(x.z) | pf.any(x.w);
         return __ballot(any != 0) != 0;
     };
 
-    // Per chunk of NV tiles: all NV loads are requested at once.  A short
+    // Chunks of NV tiles, double-buffered: the loads of chunk c+1 are in
+    // flight while chunk c is processed.  Processing a chunk: a short
     // unrolled pass waits for each tile in request order and notes which
-    // tiles have elements past the pre-filter; once the whole chunk has
-    // arrived, one rolled loop (the same code for every tile, so it is
-    // fetched once) appends their admitted elements.  After the seed no
-    // workgroup barrier is taken: waves run independently and hide each
-    // other's load latency.  A wave whose entries do not fit records the
-    // tile; phase B makes room and filters those tiles again.
-    for (u32 t0 = 0; t0 < ntiles; t0 += NV) {
-        uint4 v[NV];
-        int vb[NV];
+    // tiles have elements past the pre-filter; once the chunk has arrived,
+    // one rolled loop (the same code for every tile, so it is fetched once)
+    // appends their admitted elements.  No workgroup barrier is taken while
+    // appending: waves run independently and hide each other's load
+    // latency.  A wave whose entries do not fit records the tile; phase B
+    // makes room and filters those tiles again.
+    auto issue = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             vb[i] = t0 + (u32)i < ntiles ? v0 + (int)pr * kTileVecs : v1;
@@ -1169,12 +1232,14 @@ void topk_rows(Params p) {
             pr += a;
             if (pr >= ntiles) pr -= ntiles;
         }
-        u32 cand = 0;     // wave-uniform: tiles to append
-        u32 counted = 0;  // tiles already counted in the histogram (the seed)
-        if (t0 == 0) {
-            // Seed: count every element of the first kSeed tiles, take the
+    };
+    auto process = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV], auto seed_tag) __attribute__((always_inline)) {
+        constexpr bool kSeedChunk = decltype(seed_tag)::value;
+        u32 cand = 0;  // wave-uniform: tiles to stage
+        if constexpr (kSeedChunk) {
+            // Seed: count every element of the first kSeed tiles and take the
             // bin edge of the k-th counted as the bound; those tiles are then
-            // appended (they fit an empty buffer) without counting again.
+            // staged like the others.
 #pragma unroll
             for (int i = 0; i < kSeed; ++i) {
                 const uint4 xs[1] = {v[i]};
@@ -1191,13 +1256,14 @@ void topk_rows(Params p) {
             }
             DSTK_PHASE(19);
             __syncthreads();
-            if (tid < kWave) wave_locate(sm, k, 0u, false);
+            // the locate also clears the histogram: from here on it counts
+            // exactly the buffer's entries
+            if (tid < kWave) wave_locate(sm, k, 0u, true);
             __syncthreads();
             if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
             pf.set(L);
             DSTK_PHASE(7);
             cand = (1u << kSeed) - 1u;
-            counted = cand;
 #pragma unroll
             for (int i = kSeed; i < NV; ++i)
                 if (maybe(v[i])) cand |= 1u << i;
@@ -1206,23 +1272,40 @@ void topk_rows(Params p) {
             for (int i = 0; i < NV; ++i)
                 if (maybe(v[i])) cand |= 1u << i;
         }
-        u32 pending = 0;  // wave-uniform: tiles this wave still has to append
+        if (t0 == 2 * NV) DSTK_PHASE(29);
+        // The chunk has arrived: stage tile 0, then rotate the chunk's
+        // registers by one (every index is a constant, so the chunk stays in
+        // registers).  A wave that cannot flush stops with v[0] = the tile to
+        // resume at, and phase B finishes it.
+        u32 pending = 0;            // wave-uniform: this wave stopped early
+        u32 rtile = NV, rslot = 0;  // where to resume: tile, slot group
 #pragma unroll 1
-        for (int i = 0; i < NV; ++i) {
-            if (!((cand >> i) & 1u)) continue;
-            uint4 x = v[0];
-            int vbi = vb[0];
-#pragma unroll
-            for (int j = 1; j < NV; ++j)
-                if (i == j) {
-                    x = v[j];
-                    vbi = vb[j];
+        for (u32 i = 0; i < (u32)NV; ++i) {
+            if ((cand >> i) & 1u) {
+                u32 g = 0;
+                while (g < kGroups && stage_group(v[0], vb[0], g)) ++g;
+                if (g < kGroups) {
+                    pending = 1;
+                    rtile = i;
+                    rslot = g;
+                    break;
                 }
-            if (!filter(x, vbi, !((counted >> i) & 1u))) pending |= 1u << i;
+            }
+            const uint4 t = v[0];
+            const int tb = vb[0];
+#pragma unroll
+            for (int j = 0; j + 1 < NV; ++j) {
+                v[j] = v[j + 1];
+                vb[j] = vb[j + 1];
+            }
+            v[NV - 1] = t;
+            vb[NV - 1] = tb;
         }
+        if (!pending && !flush()) pending = 1;  // rtile = NV: only the flush is left
 
-        // Phase B (rare): make room, raise the bound, filter what did not fit.
+        // Phase B (rare): make room, raise the bound, finish what did not fit.
         DSTK_PHASE(8);
+        if (t0 == 2 * NV) DSTK_PHASE(30);
         for (int round = 0; round < 64; ++round) {
             // "any wave pending?" in one barrier: slot `par` collects the
             // answer; the other slot, last read before an earlier barrier,
@@ -1239,23 +1322,74 @@ void topk_rows(Params p) {
             if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
-            const u32 todo = pending;
+            if (!pending) continue;
             pending = 0;
-            for (int i = 0; i < NV; ++i) {
-                if ((todo >> i) & 1u) {
-                    const uint4 x = load_vec(vb[i] + (int)tid);  // cached: read moments ago
-                    if (!filter(x, vb[i], !((counted >> i) & 1u))) pending |= 1u << i;
+            if (!flush()) {
+                pending = 1;
+                continue;
+            }
+#pragma unroll 1
+            for (u32 j = rtile; j < (u32)NV; ++j) {
+                if ((cand >> j) & 1u) {
+                    u32 g = j == rtile ? rslot : 0u;
+                    while (g < kGroups && stage_group(v[0], vb[0], g)) ++g;
+                    if (g < kGroups) {
+                        pending = 1;
+                        rtile = j;
+                        rslot = g;
+                        break;
+                    }
                 }
+                const uint4 t = v[0];
+                const int tb = vb[0];
+#pragma unroll
+                for (int q = 0; q + 1 < NV; ++q) {
+                    v[q] = v[q + 1];
+                    vb[q] = vb[q + 1];
+                }
+                v[NV - 1] = t;
+                vb[NV - 1] = tb;
+            }
+            if (!pending) {
+                rtile = NV;
+                if (!flush()) pending = 1;
             }
         }
-        // Between chunks (long segments only): tidy up and raise the bound.
-        if (t0 + NV < ntiles) {
+        if (t0 == 2 * NV) DSTK_PHASE(31);
+        DSTK_PHASE(25 + (t0 / NV < 6u ? t0 / NV : 6u));
+        // Raise the bound after chunks 0, 1, 3, 7, 15, ... (a fixed schedule,
+        // so every wave takes the same barriers; the bound tightens roughly
+        // as the number of elements seen doubles).
+        const u32 c = t0 / NV;
+        if (t0 + NV < ntiles && ((c + 1) & c) == 0) {
+            __syncthreads();  // no wave appends past this point
             if (sm.count > (u32)CAP / 2) make_room<E, WG, CAP>(sm, sm.count, k, 0);
             if (tid < kWave) wave_locate(sm, k, 0u, false);
             __syncthreads();
             if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
+        }
+    };
+    {
+        // The next chunk is always requested, also past the segment's end
+        // (such tiles are range-checked buffer loads that return zeros and
+        // touch no memory), so every path has the same loads in flight and
+        // each tile waits only for its own load.
+        uint4 va[NV], vc[NV];
+        int vba[NV], vbc[NV];
+        issue(0, va, vba);
+        issue(NV, vc, vbc);
+        process(0, va, vba, std::true_type{});
+        if ((u32)NV < ntiles) {
+            for (u32 t0 = NV;; t0 += 2 * NV) {
+                issue(t0 + NV, va, vba);
+                process(t0, vc, vbc, std::false_type{});
+                if (t0 + NV >= ntiles) break;
+                issue(t0 + 2 * NV, vc, vbc);
+                process(t0 + NV, va, vba, std::false_type{});
+                if (t0 + 2 * NV >= ntiles) break;
+            }
         }
     }
     if (saw_nan) sm.nan = 1;  // benign race: every writer stores 1
@@ -1375,7 +1509,7 @@ void topk_rows(Params p) {
     for (u32 i = tid; i < S * 4; i += WG) mc[i] = ld_agent(&p.ws_meta[(u64)row * S * 4 + i]);
     for (u32 i = tid; i < S * kDirCache; i += WG)
         dc[i] = ld_agent(&rdir[(u64)(i / kDirCache) * kBins + (i % kDirCache)]);
-    for (u32 i = tid; i < kBins; i += WG) sm.hist[i] = 0;
+    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     if (tid == 0) p.ws_ticket[row] = 0;  // ready for the next call
     __syncthreads();
     DSTK_PHASE(15);
