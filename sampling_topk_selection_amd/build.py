@@ -43,6 +43,9 @@ FLAGS = [
     "-mcode-object-version=5",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels issue LDS atomics from one lane with a wave-uniform amount;
+    # the atomic optimizer would wrap each in a scan over the active lanes
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -117,24 +117,34 @@ struct PreFilter<Elem<4>> {
     __device__ u32 any(u32 d) const { return (u32)!(__uint_as_float(d) < t); }
 };
 
-// Per-slot pre-filter mask of one 16-byte vector (bit s: element s may be at
-// or above the bound; NaN always passes).  Slot order is element order.
-__device__ __forceinline__ u32 pass_mask(const PreFilter<Elem<4>>& pf, const uint4& x) {
-    return pf.any(x.x) | (pf.any(x.y) << 1) | (pf.any(x.z) << 2) | (pf.any(x.w) << 3);
+// Element s of a thread's 16-byte vector, given as its four words; s is a
+// compile-time constant at every use, so this selects registers.  Slot order
+// is element order (bf16: low half of a word first).
+template <int s>
+__device__ __forceinline__ u32 slot_bits(Elem<4>, const u32 (&dw)[4]) {
+    return dw[s];
 }
-__device__ __forceinline__ u32 pass_mask(const PreFilter<Elem<2>>& pf, const uint4& x) {
-    return pf.pass2(x.x) | (pf.pass2(x.y) << 2) | (pf.pass2(x.z) << 4) | (pf.pass2(x.w) << 6);
+template <int s>
+__device__ __forceinline__ u32 slot_bits(Elem<2>, const u32 (&dw)[4]) {
+    return (s & 1) ? (dw[s >> 1] >> 16) : (dw[s >> 1] & 0xFFFFu);
 }
-// Raw bits of element s of a 16-byte vector given as its four words (by
-// value: selecting among registers, never indexing memory).
-__device__ __forceinline__ u32 slot_bits(Elem<4>, u32 x0, u32 x1, u32 x2, u32 x3, u32 s) {
-    const u32 lo = (s & 1u) ? x1 : x0, hi = (s & 1u) ? x3 : x2;
-    return (s & 2u) ? hi : lo;
+// Pre-filter of element s: may it be at or above the bound (NaN passes)?
+template <int s>
+__device__ __forceinline__ bool pass_slot(const PreFilter<Elem<4>>& pf, const u32 (&dw)[4]) {
+    return !(__uint_as_float(dw[s]) < pf.t);
 }
-__device__ __forceinline__ u32 slot_bits(Elem<2>, u32 x0, u32 x1, u32 x2, u32 x3, u32 s) {
-    const u32 lo = (s & 2u) ? x1 : x0, hi = (s & 2u) ? x3 : x2;
-    const u32 d = (s & 4u) ? hi : lo;
-    return (d >> ((s & 1u) * 16u)) & 0xFFFFu;
+template <int s>
+__device__ __forceinline__ bool pass_slot(const PreFilter<Elem<2>>& pf, const u32 (&dw)[4]) {
+    return (s & 1) ? !(__uint_as_float(dw[s >> 1]) < pf.t_hi) : !(__uint_as_float(dw[s >> 1] << 16) < pf.t_lo);
+}
+// Is element s a NaN?  (Its value widened to fp32: a NaN stays a NaN.)
+template <int s>
+__device__ __forceinline__ bool nan_slot(Elem<4>, const u32 (&dw)[4]) {
+    return __builtin_isnan(__uint_as_float(dw[s]));
+}
+template <int s>
+__device__ __forceinline__ bool nan_slot(Elem<2>, const u32 (&dw)[4]) {
+    return __builtin_isnan(__uint_as_float((s & 1) ? (dw[s >> 1] & 0xFFFF0000u) : (dw[s >> 1] << 16)));
 }
 
 // ------------------------------------------------------------------ shared
@@ -171,7 +181,7 @@ struct Smem {
     u32 loc_total, loc_dhi;
     u32 outcount;        // emit: output slots handed out
     u32 pflag[2];        // scan: "some wave has a tile left over", two slots
-    u64 stage[8][256];   // scan: per-wave staging of pre-filter survivors (raw bits << 32 | column)
+    u32 wfill[16];       // scan: raw entries each wave has appended since the last sync
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
 #ifdef DSTK_PROBE_SLOTS
     u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
@@ -196,6 +206,28 @@ __device__ __forceinline__ u32 lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ u32 mbcnt(u64 m) {
     return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
+}
+// base + number of lanes below this one whose bit is set in m
+__device__ __forceinline__ u32 mbcnt_from(u64 m, u32 base) {
+    return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, base));
+}
+
+// Make the compiler treat x as rewritten here (no instruction is emitted), so
+// values computed from it before are not reused after.
+__device__ __forceinline__ void opaque(uint4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+__device__ __forceinline__ void opaque_s(int& x) {  // x wave-uniform
+    asm volatile("" : "+s"(x));
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 // Inclusive prefix sum across the 64 lanes (all lanes active).
@@ -562,7 +594,8 @@ __device__ __noinline__ void make_room(Smem<CAP>& sm, u32 cnt, u32 k, u32 room) 
     hist_locate<WG, CAP>(sm, k);
     const u32 d = sm.sel_digit, keep = sm.sel_above + sm.sel_c;
     if (sm.sel_c > 0 && keep + room <= (u32)CAP) {
-        const u32 kept = keep_at_least<WG, CAP>(sm, 0, cnt, digit_floor(d));
+        // (at least 1: the empty composite 0 left by an overflow never stays)
+        const u32 kept = keep_at_least<WG, CAP>(sm, 0, cnt, d > 0 ? digit_floor(d) : 1ull);
         if (tid == 0) {
             sm.count = kept;
             sm.L = digit_floor(d) > sm.L ? digit_floor(d) : sm.L;
@@ -1082,6 +1115,7 @@ void topk_rows(Params p) {
     constexpr int kTileElems = kTileVecs * E::kPerVec;
     static_assert(CAP % WG == 0, "capacity must be a multiple of the workgroup size");
     static_assert(CAP >= 2 * NV * kTileElems || NV * kTileElems >= 8192, "capacity must hold two chunks");
+    static_assert(NV <= WG / kWave, "one wave's chunk must fit in a tile of the workgroup");
     __shared__ Smem<CAP> sm;
 
     DSTK_PROBE_INIT
@@ -1130,7 +1164,6 @@ void topk_rows(Params p) {
     PreFilter<E> pf;
     u64 L = 0;
     pf.set(L);
-    bool saw_nan = false;
     __syncthreads();
 
     u32 pr = b;  // permuted index of the next tile to request
@@ -1138,80 +1171,129 @@ void topk_rows(Params p) {
     constexpr int kSeed = NV < 2 ? NV : 2;  // tiles counted to seed the bound
     static_assert(CAP >= kSeed * kTileElems, "the seed tiles must fit an empty buffer");
 
-    // Each wave stages the elements that pass the float pre-filter (raw
-    // bits and column) in its own LDS area, then flushes them 64 at a time
-    // with full lanes: decode, exact composite test against L, append and
-    // count.  The work per tile then follows the admissions, not the tile
-    // size, and ties with the bound's value (long runs of equal values) are
-    // filtered densely.
-    constexpr u32 kStageCap = 256;
-    static_assert(sizeof(sm.stage[0]) / sizeof(u64) == kStageCap && WG / kWave <= 8, "stage layout");
-    u64* const stage = sm.stage[tid / kWave];
-    u32 sbeg = 0, send = 0;  // wave-uniform: this wave's staged window
-    // Returns false, leaving the unflushed batch staged, when it does not fit.
-    auto flush = [&]() __attribute__((always_inline)) -> bool {
-        for (; sbeg < send; sbeg += kWave) {
-            const u32 i = sbeg + lane_id();
-            const bool in = i < send;
-            const u64 st = in ? stage[i] : 0ull;
-            const u32 bits = (u32)(st >> 32);
-            saw_nan |= in && E::is_nan(bits);
-            const u64 e = compose<E>(E::key(bits), (u32)st);
-            const bool ok = in && e >= L;
-            const u64 m = __ballot(ok);
-            if (m == 0) continue;
-            const u32 base = wave_reserve_base(&sm.count, (u32)__popcll(m), (u32)CAP);
-            if (base == kFull) return false;  // uniform: the batch stays staged
-            if (ok) {
-                sm.buf[base + mbcnt(m)] = e;
-                atomicAdd(&sm.hist[hidx(top_digit(e))], 1u);
+    // ---- buffer layout while scanning.  buf[0, cbase) holds composites,
+    // counted in the histogram.  The free part is split into one region of
+    // R entries per wave; a wave appends raw entries (element bits << 32 |
+    // column) to its own region behind a scalar write pointer, with no
+    // atomics and no barrier.  A sync moves the regions' entries behind the
+    // composites, converting and counting them with every lane busy.
+    constexpr u32 kWaves = WG / kWave;
+    const u32 wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
+    u32 cbase = 0, R = (u32)CAP / kWaves;  // wave-uniform
+    u32 wp = wave_u * R, re = wp + R;       // this wave's write pointer and region end
+    auto assign_regions = [&](u32 cnt) __attribute__((always_inline)) {
+        cbase = cnt;
+        R = ((u32)CAP - cnt) / kWaves;
+        wp = cnt + wave_u * R;
+        re = wp + R;
+    };
+    // Call before the barrier that precedes a sync.
+    auto note_fill = [&]() __attribute__((always_inline)) {
+        if (lane_id() == 0) sm.wfill[wave_u] = wp - (cbase + wave_u * R);
+    };
+    bool saw_nan = false;  // per lane
+    // Move, convert and count; returns the new number of composites.  Entry j
+    // of the regions' concatenation goes to cbase + j, at or below where it
+    // is, and every batch is read before it is written, so no entry is
+    // overwritten before it has been read.
+    auto sync_buffer = [&]() __attribute__((always_inline)) -> u32 {
+        u32 fill[kWaves], off[kWaves], N = 0;
+#pragma unroll
+        for (u32 w = 0; w < kWaves; ++w) {
+            fill[w] = __builtin_amdgcn_readfirstlane(sm.wfill[w]);
+            off[w] = N;
+            N += fill[w];
+        }
+        constexpr u32 kB = 4;
+        for (u32 base = 0; base < N; base += WG * kB) {
+            u64 e[kB];
+#pragma unroll
+            for (u32 i = 0; i < kB; ++i) {
+                const u32 j = base + i * WG + tid;
+                e[i] = 0;
+                if (j < N) {
+                    u32 w = 0;
+#pragma unroll
+                    for (u32 q = 1; q < kWaves; ++q) w = j >= off[q] ? q : w;
+                    const u64 raw = sm.buf[cbase + w * R + (j - off[w])];
+                    const u32 bits = (u32)(raw >> 32);
+                    saw_nan |= E::is_nan(bits);
+                    e[i] = compose<E>(E::key(bits), (u32)raw);
+                }
             }
-        }
-        sbeg = send = 0;
-        return true;
-    };
-    // Stage the pre-filter survivors of group g (slots 4g .. 4g+3) of one
-    // tile: each lane writes its survivors behind a wave prefix sum, in
-    // straight-line code.  Returns false when the stage cannot take them
-    // and cannot be flushed.
-    constexpr u32 kGroups = (u32)E::kPerVec / 4u;
-    auto stage_group = [&](const uint4 x, int vbi, u32 g) __attribute__((always_inline)) -> bool {
-        const u32 x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
-        const int vi = vbi + (int)tid;
-        u32 pm = (pass_mask(pf, x) >> (4u * g)) & 0xFu;
-        if (!(vbi + kTileVecs <= v1 && (u32)(vbi + kTileVecs) * E::kPerVec <= n)) {
-            // the tile runs past the valid columns: mask the invalid slots
-            u32 vm = 0;
+            __syncthreads();
 #pragma unroll
-            for (u32 q = 0; q < 4u; ++q)
-                vm |= (u32)(vi < v1 && (u32)vi * E::kPerVec + 4u * g + q < n) << q;
-            pm &= vm;
+            for (u32 i = 0; i < kB; ++i) {
+                const u32 j = base + i * WG + tid;
+                if (j < N) {
+                    sm.buf[cbase + j] = e[i];
+                    atomicAdd(&sm.hist[hidx(top_digit(e[i]))], 1u);
+                }
+            }
+            __syncthreads();
         }
-        // one ballot per slot: slot q's survivors go behind those of the
-        // slots before it (independent, short dependency chains)
-        u64 b[4];
-        u32 o[4];
+        return cbase + N;
+    };
+
+    // ---- admission.  One ballot per element slot gives the wave's
+    // pre-filter survivors as scalar masks, so every branch is on a scalar.
+    // In exact mode (entered once the buffer has overflowed) the survivors
+    // are also tested against the composite bound, so long runs of values
+    // equal to the bound's value cannot refill the buffer.
+    bool exact = false;        // wave-uniform
+    constexpr int P = E::kPerVec;
+    // Appends one tile's survivors; false (nothing appended) when they do not
+    // fit in the wave's region.
+    auto append_tile = [&](const uint4& x, const int vb) __attribute__((always_inline)) -> bool {
+        const u32 dw[4] = {x.x, x.y, x.z, x.w};
+        const u32 vi = (u32)(vb + (int)tid);
+        u64 m[P];
+        u64 any = 0;
+        static_for<P>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            m[s] = __ballot(pass_slot<s>(pf, dw));
+            any |= m[s];
+        });
+        if (any == 0) return true;
+        if (!(vb + kTileVecs <= v1 && (u32)(vb + kTileVecs) * P <= n)) {
+            // the tile runs past the valid columns
+            static_for<P>([&](auto S_) {
+                constexpr int s = decltype(S_)::value;
+                m[s] &= __ballot((int)vi < v1 && vi * P + s < n);
+            });
+        }
+        if (exact) {
+            static_for<P>([&](auto S_) {
+                constexpr int s = decltype(S_)::value;
+                if (m[s]) {
+                    // (a NaN passes the pre-filter; note it before the exact test)
+                    saw_nan |= ((m[s] >> lane_id()) & 1u) && nan_slot<s>(E{}, dw);
+                    m[s] &= __ballot(compose<E>(E::key(slot_bits<s>(E{}, dw)), vi * P + s) >= L);
+                }
+            });
+        }
         u32 tot = 0;
-#pragma unroll
-        for (u32 q = 0; q < 4u; ++q) {
-            b[q] = __ballot((pm >> q) & 1u);
-            o[q] = tot;
-            tot += (u32)__popcll(b[q]);
-        }
-        if (tot == 0) return true;
-        if (send + tot > kStageCap && !flush()) return false;
-        const u32 col0 = (u32)vi * E::kPerVec + 4u * g;
-#pragma unroll
-        for (u32 q = 0; q < 4u; ++q)
-            if ((pm >> q) & 1u)
-                stage[send + o[q] + mbcnt(b[q])] = ((u64)slot_bits(E{}, x0, x1, x2, x3, 4u * g + q) << 32) | (col0 + q);
-        send += tot;
+        static_for<P>([&](auto S_) { tot += (u32)__popcll(m[decltype(S_)::value]); });
+        if (wp + tot > re) return false;
+        static_for<P>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            if (m[s]) {
+                if (__builtin_amdgcn_inverse_ballot_w64(m[s]))
+                    sm.buf[mbcnt_from(m[s], wp)] = ((u64)slot_bits<s>(E{}, dw) << 32) | (vi * P + s);
+                wp += (u32)__popcll(m[s]);
+            }
+        });
         return true;
     };
-    // Does any element of the tile pass the float pre-filter (wave-uniform)?
-    auto maybe = [&](const uint4& x) __attribute__((always_inline)) -> bool {
-        const u32 any = pf.any(x.x) | pf.any(x.y) | pf.any(x.z) | pf.any(x.w);
-        return __ballot(any != 0) != 0;
+    // Appends tiles from..NV-1 of a chunk (constant register indices);
+    // returns the first tile that did not fit, or NV.
+    auto append_chunk = [&](const uint4 (&v)[NV], const int (&vb)[NV], u32 from) __attribute__((always_inline)) -> u32 {
+        u32 stop = (u32)NV;
+        static_for<NV>([&](auto I_) {
+            constexpr int i = decltype(I_)::value;
+            if (stop == (u32)NV && (u32)i >= from && !append_tile(v[i], vb[i])) stop = (u32)i;
+        });
+        return stop;
     };
 
     // Chunks of NV tiles, double-buffered: the loads of chunk c+1 are in
@@ -1233,164 +1315,111 @@ void topk_rows(Params p) {
             if (pr >= ntiles) pr -= ntiles;
         }
     };
-    auto process = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV], auto seed_tag) __attribute__((always_inline)) {
-        constexpr bool kSeedChunk = decltype(seed_tag)::value;
-        u32 cand = 0;  // wave-uniform: tiles to stage
-        if constexpr (kSeedChunk) {
-            // Seed: count every element of the first kSeed tiles and take the
-            // bin edge of the k-th counted as the bound; those tiles are then
-            // staged like the others.
+    // Seed: count every element of the first kSeed tiles and take the bin
+    // edge of the k-th counted as the bound; those tiles are then appended
+    // like the others.
+    auto seed = [&](const uint4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < kSeed; ++i) {
-                const uint4 xs[1] = {v[i]};
+        for (int i = 0; i < kSeed; ++i) {
+            const uint4 xs[1] = {v[i]};
 #pragma unroll
-                for (int s = 0; s < SL::kSlots; ++s) {
-                    u32 bits, col;
-                    bool valid;
-                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
-                    if (valid) {
-                        saw_nan |= E::is_nan(bits);
-                        atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(bits), col)))], 1u);
-                    }
-                }
+            for (int s = 0; s < SL::kSlots; ++s) {
+                u32 bits, col;
+                bool valid;
+                SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                if (valid) atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(bits), col)))], 1u);
             }
-            DSTK_PHASE(19);
-            __syncthreads();
-            // the locate also clears the histogram: from here on it counts
-            // exactly the buffer's entries
-            if (tid < kWave) wave_locate(sm, k, 0u, true);
-            __syncthreads();
-            if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
-            pf.set(L);
-            DSTK_PHASE(7);
-            cand = (1u << kSeed) - 1u;
-#pragma unroll
-            for (int i = kSeed; i < NV; ++i)
-                if (maybe(v[i])) cand |= 1u << i;
-        } else {
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (maybe(v[i])) cand |= 1u << i;
         }
+        DSTK_PHASE(19);
+        __syncthreads();
+        // the locate also clears the histogram: from here on it counts
+        // exactly the synced entries
+        if (tid < kWave) wave_locate(sm, k, 0u, true);
+        __syncthreads();
+        if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
+        pf.set(L);
+        DSTK_PHASE(7);
+    };
+    // Append a chunk.  When a region is full (rare): sync, make room if the
+    // buffer is short of a whole tile of the workgroup, raise the bound and
+    // resume.  With that much room every region holds one wave's tile, so
+    // each round appends at least one tile of every waiting wave and at most
+    // NV + 1 rounds are taken.  After chunks 0, 1, 3, 7, 15, ... (a fixed
+    // schedule, so every wave takes the same barriers; the bound tightens
+    // roughly as the number of elements seen doubles) the same step syncs
+    // and raises the bound without a resume.
+    auto process = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
         if (t0 == 2 * NV) DSTK_PHASE(29);
-        // The chunk has arrived: stage tile 0, then rotate the chunk's
-        // registers by one (every index is a constant, so the chunk stays in
-        // registers).  A wave that cannot flush stops with v[0] = the tile to
-        // resume at, and phase B finishes it.
-        u32 pending = 0;            // wave-uniform: this wave stopped early
-        u32 rtile = NV, rslot = 0;  // where to resume: tile, slot group
-#pragma unroll 1
-        for (u32 i = 0; i < (u32)NV; ++i) {
-            if ((cand >> i) & 1u) {
-                u32 g = 0;
-                while (g < kGroups && stage_group(v[0], vb[0], g)) ++g;
-                if (g < kGroups) {
-                    pending = 1;
-                    rtile = i;
-                    rslot = g;
-                    break;
-                }
-            }
-            const uint4 t = v[0];
-            const int tb = vb[0];
+        const u32 c = t0 / NV;
+        const bool raise = t0 + NV < ntiles && ((c + 1) & c) == 0;
+        u32 rtile = 0;  // wave-uniform: first tile not appended yet, or NV
+        for (u32 round = 0;; ++round) {
+            // (keeps the exact-mode and resume work inside the rounds rather
+            // than hoisted in front of the common first round)
 #pragma unroll
-            for (int j = 0; j + 1 < NV; ++j) {
-                v[j] = v[j + 1];
-                vb[j] = vb[j + 1];
+            for (int i = 0; i < NV; ++i) {
+                opaque(v[i]);
+                opaque_s(vb[i]);
             }
-            v[NV - 1] = t;
-            vb[NV - 1] = tb;
-        }
-        if (!pending && !flush()) pending = 1;  // rtile = NV: only the flush is left
-
-        // Phase B (rare): make room, raise the bound, finish what did not fit.
-        DSTK_PHASE(8);
-        if (t0 == 2 * NV) DSTK_PHASE(30);
-        for (int round = 0; round < 64; ++round) {
-            // "any wave pending?" in one barrier: slot `par` collects the
+            if (rtile < (u32)NV) rtile = append_chunk(v, vb, rtile);
+            if (t0 == 2 * NV && round == 0) DSTK_PHASE(30);
+            // "any wave left over?" in one barrier: slot `par` collects the
             // answer; the other slot, last read before an earlier barrier,
-            // is cleared for the next check
-            if (lane_id() == 0 && pending) atomicOr(&sm.pflag[par], 1u);
+            // is cleared for the next check.  The barrier also follows every
+            // wave's last append and fill note, as a sync needs.
+            if (lane_id() == 0 && rtile < (u32)NV) atomicOr(&sm.pflag[par], 1u);
             if (tid == 0) sm.pflag[par ^ 1u] = 0;
+            note_fill();
             __syncthreads();
             const bool again = sm.pflag[par] != 0;
             par ^= 1u;
-            if (!again) break;
-            make_room<E, WG, CAP>(sm, sm.count, k, kTileElems);
+            if (!again && !(raise && round == 0)) break;
+            if (round > (u32)NV) {  // unreachable: the room argument above
+                saw_nan = true;  // reported as an invalid result, never silently
+                break;
+            }
+            const u32 cnt = sync_buffer();
+            if (again ? cnt > (u32)(CAP - kTileElems) : (cnt > (u32)CAP / 2 && cnt > k)) {
+                make_room<E, WG, CAP>(sm, cnt, k, again ? (u32)kTileElems : 0u);
+            } else {
+                if (tid == 0) sm.count = cnt;
+            }
+            exact = exact || again;
             if (tid < kWave) wave_locate(sm, k, 0u, false);
             __syncthreads();
             if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
-            if (!pending) continue;
-            pending = 0;
-            if (!flush()) {
-                pending = 1;
-                continue;
-            }
-#pragma unroll 1
-            for (u32 j = rtile; j < (u32)NV; ++j) {
-                if ((cand >> j) & 1u) {
-                    u32 g = j == rtile ? rslot : 0u;
-                    while (g < kGroups && stage_group(v[0], vb[0], g)) ++g;
-                    if (g < kGroups) {
-                        pending = 1;
-                        rtile = j;
-                        rslot = g;
-                        break;
-                    }
-                }
-                const uint4 t = v[0];
-                const int tb = vb[0];
-#pragma unroll
-                for (int q = 0; q + 1 < NV; ++q) {
-                    v[q] = v[q + 1];
-                    vb[q] = vb[q + 1];
-                }
-                v[NV - 1] = t;
-                vb[NV - 1] = tb;
-            }
-            if (!pending) {
-                rtile = NV;
-                if (!flush()) pending = 1;
-            }
+            assign_regions(__builtin_amdgcn_readfirstlane(sm.count));
+            if (!again) break;
         }
         if (t0 == 2 * NV) DSTK_PHASE(31);
-        DSTK_PHASE(25 + (t0 / NV < 6u ? t0 / NV : 6u));
-        // Raise the bound after chunks 0, 1, 3, 7, 15, ... (a fixed schedule,
-        // so every wave takes the same barriers; the bound tightens roughly
-        // as the number of elements seen doubles).
-        const u32 c = t0 / NV;
-        if (t0 + NV < ntiles && ((c + 1) & c) == 0) {
-            __syncthreads();  // no wave appends past this point
-            if (sm.count > (u32)CAP / 2) make_room<E, WG, CAP>(sm, sm.count, k, 0);
-            if (tid < kWave) wave_locate(sm, k, 0u, false);
-            __syncthreads();
-            if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
-            if (sm.L > L) L = sm.L;
-            pf.set(L);
-        }
+        DSTK_PHASE(25 + (c < 6u ? c : 6u));
     };
     {
-        // The next chunk is always requested, also past the segment's end
-        // (such tiles are range-checked buffer loads that return zeros and
-        // touch no memory), so every path has the same loads in flight and
-        // each tile waits only for its own load.
+        // Double buffering: chunk c + 1 is in flight while chunk c is
+        // appended.  The next chunk is always requested, also past the
+        // segment's end (such tiles are range-checked buffer loads that
+        // return zeros and touch no memory), so every path has the same loads
+        // in flight and each tile waits only for its own load.
         uint4 va[NV], vc[NV];
         int vba[NV], vbc[NV];
         issue(0, va, vba);
         issue(NV, vc, vbc);
-        process(0, va, vba, std::true_type{});
-        if ((u32)NV < ntiles) {
-            for (u32 t0 = NV;; t0 += 2 * NV) {
-                issue(t0 + NV, va, vba);
-                process(t0, vc, vbc, std::false_type{});
-                if (t0 + NV >= ntiles) break;
-                issue(t0 + 2 * NV, vc, vbc);
-                process(t0 + NV, va, vba, std::false_type{});
-                if (t0 + 2 * NV >= ntiles) break;
-            }
+        seed(va, vba);
+        for (u32 t0 = 0;; t0 += 2 * NV) {
+            process(t0, va, vba);
+            if (t0 + NV >= ntiles) break;
+            issue(t0 + 2 * NV, va, vba);
+            process(t0 + NV, vc, vbc);
+            if (t0 + 2 * NV >= ntiles) break;
+            issue(t0 + 3 * NV, vc, vbc);
         }
+    }
+    {
+        // the last check's barrier follows every wave's last append
+        const u32 cnt = sync_buffer();
+        if (tid == 0) sm.count = cnt;
     }
     if (saw_nan) sm.nan = 1;  // benign race: every writer stores 1
     if (tid == 0) sm.L = L;
