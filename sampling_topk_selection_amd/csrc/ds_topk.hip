@@ -21,6 +21,7 @@ constexpr int kVersion = 100;       // 0.1.0
 constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS count each)
 constexpr int kTargetWG = 256;      // one workgroup per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
+constexpr int64_t kMinSegElems = 8192;  // and at least this many: below it the merge costs more than it saves
 #ifndef DS_TOPK_TILES_PER_CHUNK
 #define DS_TOPK_TILES_PER_CHUNK 4
 #endif
@@ -92,6 +93,8 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
         s = batch >= kTargetWG ? 1 : (kTargetWG + batch - 1) / (batch > 0 ? batch : 1);
         const int64_t by_k = n / ((int64_t)kSegPerK * k);
         if (s > by_k) s = by_k;
+        const int64_t by_size = n / kMinSegElems;
+        if (s > by_size) s = by_size;
     }
     if (s > kMaxSegs) s = kMaxSegs;
     if (s > pl->n_vec) s = pl->n_vec;

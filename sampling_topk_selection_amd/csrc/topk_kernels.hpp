@@ -153,10 +153,9 @@ constexpr int kBins = 1 << kHistBits;
 constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
 
 // Histogram storage is transposed with a padded row: bin d lives at
-// ((d mod 32) * 65 + d / 32).  The 32 consecutive bins one lane owns in
-// wave_locate form a column that it reads with immediate offsets from one
-// address; a row read by 64 lanes, and atomics on consecutive bins (the hot
-// bins next to the bound), hit distinct banks.
+// ((d mod 32) * 65 + d / 32), so atomics on consecutive bins (the hot bins
+// next to the bound) and reads of runs of bins by consecutive lanes hit
+// distinct banks.
 constexpr int kHistRow = 65;
 constexpr int kHistWords = 32 * kHistRow;
 __device__ __forceinline__ u32 hidx(u32 d) { return (d & 31u) * (u32)kHistRow + (d >> 5); }
@@ -182,6 +181,8 @@ struct Smem {
     u32 outcount;        // emit: output slots handed out
     u32 pflag[2];        // scan: "some wave has a tile left over", two slots
     u32 wfill[16];       // scan: raw entries each wave has appended since the last sync
+    u32 lwsum[16];       // block_locate: per-wave bin totals
+    u32 lwfirst[16];     // block_locate: per-wave first thread with a non-empty bin, or 64
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
 #ifdef DSTK_PROBE_SLOTS
     u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
@@ -732,68 +733,81 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
 // ------------------------------------------------------------------ selection by threshold
 __device__ __forceinline__ u64 low_mask(int b) { return b >= 64 ? ~0ull : ((1ull << b) - 1ull); }
 
-// Run by one whole wave while the others wait at the caller's next barrier.
-// Lane l owns histogram bins [kBins - 32 (l + 1), kBins - 32 l), so lane 0
-// holds the highest.  For ranks r0 and r1 (r >= 1; 0 = not wanted) it finds
-// the bin holding the r-th largest counted entry and leaves loc_digit,
-// loc_r (rank inside the bin), loc_c (bin count, 0 when fewer than r are
-// counted) and loc_above (entries in higher bins); also loc_total and
-// loc_dhi (highest non-empty bin).  zero: clear the histogram afterwards.
-template <int CAP>
-__device__ __noinline__ void wave_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero) {
-    const u32 l = lane_id();
-    u32* hc = sm.hist + (63u - l);  // this lane's bins, kBins - 32 (l + 1) + j, at hc[kHistRow j]
+// For ranks r0 and r1 (r >= 1; 0 = not wanted): the bin holding the r-th
+// largest counted entry, as loc_digit, loc_r (rank inside the bin), loc_c
+// (bin count; 0 when fewer than r are counted) and loc_above (entries in
+// higher bins); also loc_total and loc_dhi (highest non-empty bin, 0 if
+// none).  The whole workgroup takes part: thread t owns the kBins / WG bins
+// just below kBins - t kBins / WG (descending bin order is thread order), a
+// wave scan and one exchange of wave totals give every thread the entries in
+// higher bins, and the thread whose bins hold rank r writes the result.
+// Call from every thread; returns after a barrier, with the results visible
+// to all.  With `zero` the histogram is cleared on the way.
+template <int WG, int CAP>
+__device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero) {
+    constexpr u32 kPer = kBins / WG;
+    constexpr u32 kW = WG / kWave;
+    static_assert(kPer * WG == kBins && kW <= 16, "bins per thread");
+    const u32 tid = threadIdx.x, wave = tid / kWave, l = lane_id();
+    u32 c[kPer];
     u32 s = 0;
 #pragma unroll
-    for (u32 j = 0; j < 32; ++j) s += hc[kHistRow * j];
-    const u32 incl = wave_incl_scan(s);
-    const u32 excl = incl - s;
-    if (l == 63) sm.loc_total = incl;
-    // Second step inside one lane's 32 bins, spread over the wave: lane i
-    // (< 32) takes bin lo(f) + 31 - i, so lane order is descending bin order.
-    const u32 i32 = l & 31u;
-    const u64 nz = __ballot(s != 0);
-    if (nz == 0) {
-        if (l == 0) sm.loc_dhi = 0;
-    } else {
-        const u32 f = (u32)__builtin_ctzll(nz);
-        const u32 flo = kBins - 32u * (f + 1u);
-        const u32 c = l < 32 ? sm.hist[hidx(flo + 31u - i32)] : 0u;
-        const u64 m = __ballot(c != 0);
-        if (l == 0) sm.loc_dhi = flo + 31u - (u32)__builtin_ctzll(m);
+    for (u32 j = 0; j < kPer; ++j) {
+        u32* h = &sm.hist[hidx(kBins - 1u - (tid * kPer + j))];
+        c[j] = *h;
+        s += c[j];
+        if (zero) *h = 0;
     }
+    const u32 incl = wave_incl_scan(s);
+    const u64 nz = __ballot(s != 0);
+    if (l == kWave - 1) sm.lwsum[wave] = incl;
+    if (l == 0) sm.lwfirst[wave] = nz ? (u32)__builtin_ctzll(nz) : (u32)kWave;
+    __syncthreads();
+    u32 off = 0, tot = 0, fw = kW;
+#pragma unroll
+    for (u32 w = 0; w < kW; ++w) {
+        const u32 v = sm.lwsum[w];
+        off += w < wave ? v : 0u;
+        tot += v;
+        fw = (fw == kW && v != 0) ? w : fw;
+    }
+    const u32 excl = off + incl - s;  // entries in bins above this thread's
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const u32 r = q == 0 ? r0 : r1;
         if (r == 0) continue;
-        const u64 m = __ballot(excl < r && r <= incl);
-        if (m == 0) {
-            if (l == 0) {
+        if (r > tot) {
+            if (tid == 0) {
                 sm.loc_digit[q] = 0;
                 sm.loc_r[q] = 0;
                 sm.loc_c[q] = 0;
                 sm.loc_above[q] = 0;
             }
-            continue;
-        }
-        const u32 f = (u32)__builtin_ctzll(m);
-        const u32 flo = kBins - 32u * (f + 1u);
-        const u32 base = __builtin_amdgcn_readlane(excl, f);
-        const u32 c = l < 32 ? sm.hist[hidx(flo + 31u - i32)] : 0u;
-        const u32 ci = wave_incl_scan(c);  // lanes >= 32 add nothing
-        const u32 ce = base + ci - c;      // entries in higher bins
-        const u64 hit = __ballot(l < 32 && ce < r && r <= ce + c);
-        if (l == (u32)__builtin_ctzll(hit)) {
-            sm.loc_digit[q] = flo + 31u - i32;
-            sm.loc_r[q] = r - ce;
-            sm.loc_c[q] = c;
-            sm.loc_above[q] = ce;
-        }
-    }
-    if (zero) {
+        } else if (excl < r && r <= excl + s) {
+            u32 above = excl;
 #pragma unroll
-        for (u32 j = 0; j < 32; ++j) hc[kHistRow * j] = 0;
+            for (u32 j = 0; j < kPer; ++j) {
+                if (above < r && r <= above + c[j]) {
+                    sm.loc_digit[q] = kBins - 1u - (tid * kPer + j);
+                    sm.loc_r[q] = r - above;
+                    sm.loc_c[q] = c[j];
+                    sm.loc_above[q] = above;
+                }
+                above += c[j];
+            }
+        }
     }
+    if (tid == 0) sm.loc_total = tot;
+    if (fw == kW) {
+        if (tid == 0) sm.loc_dhi = 0;
+    } else if (wave == fw && l == sm.lwfirst[fw]) {
+        u32 d = 0;
+#pragma unroll
+        for (int j = (int)kPer - 1; j >= 0; --j)
+            if (c[j]) d = kBins - 1u - (tid * kPer + (u32)j);
+        sm.loc_dhi = d;
+    }
+    __syncthreads();
 }
 
 // The threshold T with exactly k entries of buf[0, cnt) at or above it,
@@ -848,8 +862,7 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
             if ((e & pm) == P) atomicAdd(&sm.hist[hidx((u32)(e >> sh) & (kBins - 1))], 1u);
         }
         __syncthreads();
-        if (wave == 0) wave_locate(sm, r, 0u, true);
-        __syncthreads();
+        block_locate<WG, CAP>(sm, r, 0u, true);
         const u32 d = sm.loc_digit[0], rr = sm.loc_r[0], c = sm.loc_c[0];
         P |= (u64)d << sh;
         DSTK_PHASE(21);
@@ -885,8 +898,7 @@ __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u3
     cnt = keep_at_least<WG, CAP>(sm, 0, cnt, T);
     if (tid == 0) sm.kth = T;
     rebuild_hist<WG, CAP>(sm, cnt);
-    if (tid / kWave == 0) wave_locate(sm, k, q, false);
-    __syncthreads();
+    block_locate<WG, CAP>(sm, k, q, false);
     return cnt;
 }
 
@@ -1275,13 +1287,12 @@ void topk_rows(Params p) {
         u32 tot = 0;
         static_for<P>([&](auto S_) { tot += (u32)__popcll(m[decltype(S_)::value]); });
         if (wp + tot > re) return false;
+        // (no branch per slot: with an empty mask the writes are no-ops)
         static_for<P>([&](auto S_) {
             constexpr int s = decltype(S_)::value;
-            if (m[s]) {
-                if (__builtin_amdgcn_inverse_ballot_w64(m[s]))
-                    sm.buf[mbcnt_from(m[s], wp)] = ((u64)slot_bits<s>(E{}, dw) << 32) | (vi * P + s);
-                wp += (u32)__popcll(m[s]);
-            }
+            if (__builtin_amdgcn_inverse_ballot_w64(m[s]))
+                sm.buf[mbcnt_from(m[s], wp)] = ((u64)slot_bits<s>(E{}, dw) << 32) | (vi * P + s);
+            wp += (u32)__popcll(m[s]);
         });
         return true;
     };
@@ -1334,8 +1345,7 @@ void topk_rows(Params p) {
         __syncthreads();
         // the locate also clears the histogram: from here on it counts
         // exactly the synced entries
-        if (tid < kWave) wave_locate(sm, k, 0u, true);
-        __syncthreads();
+        block_locate<WG, CAP>(sm, k, 0u, true);
         if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
         pf.set(L);
         DSTK_PHASE(7);
@@ -1385,8 +1395,7 @@ void topk_rows(Params p) {
                 if (tid == 0) sm.count = cnt;
             }
             exact = exact || again;
-            if (tid < kWave) wave_locate(sm, k, 0u, false);
-            __syncthreads();
+            block_locate<WG, CAP>(sm, k, 0u, false);
             if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
             if (sm.L > L) L = sm.L;
             pf.set(L);
@@ -1432,8 +1441,7 @@ void topk_rows(Params p) {
     void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr;
 
     if (p.segs == 1) {
-        if (wave == 0) wave_locate(sm, k, 0u, true);
-        __syncthreads();
+        block_locate<WG, CAP>(sm, k, 0u, true);
         DSTK_PHASE(2);
         select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, n, p.sorted, p.retval,
                                     p.flags, row_idx, row_val, p.flag, p.flag_value);
@@ -1451,9 +1459,8 @@ void topk_rows(Params p) {
         // q = ceil(k / S): with every segment holding q entries at or above
         // its q-bound, the smallest q-bound over the row is a valid bound too
         const u32 q = (k + S - 1) / S;
-        if (wave == 0) wave_locate(sm, k, q, false);
+        block_locate<WG, CAP>(sm, k, q, false);
         DSTK_PHASE(11);
-        __syncthreads();
         u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
         u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
         u64 bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
@@ -1583,8 +1590,7 @@ void topk_rows(Params p) {
     }
     __syncthreads();
     DSTK_PHASE(17);
-    if (wave == 0) wave_locate(sm, k, 0u, true);
-    __syncthreads();
+    block_locate<WG, CAP>(sm, k, 0u, true);
     const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0];
     DSTK_PHASE(18);
     // entries each segment contributes: those with digit >= b1, a prefix of its list
