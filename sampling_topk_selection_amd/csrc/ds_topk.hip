@@ -22,10 +22,17 @@ constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS c
 constexpr int kTargetWG = 256;      // one workgroup per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
 constexpr int64_t kMinSegElems = 8192;  // and at least this many: below it the merge costs more than it saves
-#ifndef DS_TOPK_TILES_PER_CHUNK
-#define DS_TOPK_TILES_PER_CHUNK 4
+// Tiles per chunk (16-byte loads in flight per thread and buffer), per
+// element width: a bf16 tile holds twice the elements of an fp32 one, and
+// its eight slots per vector take more registers to filter.
+#ifndef DS_TOPK_TILES_PER_CHUNK_F32
+#define DS_TOPK_TILES_PER_CHUNK_F32 4
 #endif
-constexpr int kLoadsPerThread = DS_TOPK_TILES_PER_CHUNK;  // tiles per chunk: 16-byte loads in flight per thread
+#ifndef DS_TOPK_TILES_PER_CHUNK_BF16
+#define DS_TOPK_TILES_PER_CHUNK_BF16 2
+#endif
+constexpr int kChunkF32 = DS_TOPK_TILES_PER_CHUNK_F32;
+constexpr int kChunkBf16 = DS_TOPK_TILES_PER_CHUNK_BF16;
 constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
 
 thread_local std::string g_err;
@@ -80,7 +87,7 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     pl->eb = dtype == DS_DTYPE_BF16 ? 2 : 4;
     const int epv = 16 / pl->eb;
     pl->wg = 512;
-    pl->vpt = kLoadsPerThread;  // 16-byte loads in flight per thread (one chunk)
+    pl->vpt = pl->eb == 2 ? kChunkBf16 : kChunkF32;  // 16-byte loads in flight per thread (one chunk)
     pl->depth = 0;
     pl->cap = k <= 1024 ? 8192 : 16384;
     pl->pub_cap = 2 * k + 1024 < pl->cap ? 2 * k + 1024 : pl->cap;
@@ -209,11 +216,11 @@ hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
 hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s) {
     const int64_t grid = rows * pl.segs;
     if (pl.eb == 2) {
-        if (pl.cap == 8192) return launch_one<2, 512, kLoadsPerThread, 8192>(prm, grid, s);
-        return launch_one<2, 512, kLoadsPerThread, 16384>(prm, grid, s);
+        if (pl.cap == 8192) return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
+        return launch_one<2, 512, kChunkBf16, 16384>(prm, grid, s);
     }
-    if (pl.cap == 8192) return launch_one<4, 512, kLoadsPerThread, 8192>(prm, grid, s);
-    return launch_one<4, 512, kLoadsPerThread, 16384>(prm, grid, s);
+    if (pl.cap == 8192) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
+    return launch_one<4, 512, kChunkF32, 16384>(prm, grid, s);
 }
 
 int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,

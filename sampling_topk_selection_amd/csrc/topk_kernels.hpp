@@ -36,6 +36,15 @@ namespace dstk {
 
 using u32 = uint32_t;
 using u64 = uint64_t;
+// One 16-byte vector as the hardware loads it: kept whole in registers (a
+// four-register tuple), so a load's destination is the register the scan
+// reads, also across loop iterations.
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+// The first vector index of each tile of a chunk, passed by value.
+template <int NV>
+struct VecBases {
+    int b[NV];
+};
 
 constexpr int kWave = 64;
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle,
@@ -183,6 +192,7 @@ struct Smem {
     u32 wfill[16];       // scan: raw entries each wave has appended since the last sync
     u32 lwsum[16];       // block_locate: per-wave bin totals
     u32 lwfirst[16];     // block_locate: per-wave first thread with a non-empty bin, or 64
+    u64 trash[64];       // scan: written by the lanes that append nothing
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
 #ifdef DSTK_PROBE_SLOTS
     u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
@@ -213,13 +223,31 @@ __device__ __forceinline__ u32 mbcnt_from(u64 m, u32 base) {
     return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, base));
 }
 
-// Make the compiler treat x as rewritten here (no instruction is emitted), so
-// values computed from it before are not reused after.
-__device__ __forceinline__ void opaque(uint4& x) {
-    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+// A copy of x in a register of its own (one v_mov).  A 64-bit store of x
+// and another value needs them in an aligned register pair; without the
+// copy the compiler may place x there, and then keeps loaded vectors in
+// split registers, copying them out of each load's destination (which
+// waits for the load).
+__device__ __forceinline__ u32 fresh_copy(u32 x) {
+    u32 y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
 }
-__device__ __forceinline__ void opaque_s(int& x) {  // x wave-uniform
-    asm volatile("" : "+s"(x));
+
+// Count bin d of each lane with `valid` in hist.  When all of them fall in
+// one bin (runs of equal values: the padding of short rows, quantized
+// scores) one atomic adds them all; 64 atomics on one address would be
+// serialized.
+__device__ __forceinline__ void hist_add(u32* hist, u32 d, bool valid) {
+    const u64 act = __ballot(valid);
+    if (act == 0) return;
+    const u32 lead = (u32)__builtin_ctzll(act);
+    const u32 first = __builtin_amdgcn_readlane(d, lead);
+    if (__ballot(valid && d == first) == act) {
+        if (__lane_id() == lead) atomicAdd(&hist[hidx(first)], (u32)__popcll(act));
+    } else if (valid) {
+        atomicAdd(&hist[hidx(d)], 1u);
+    }
 }
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
@@ -583,7 +611,10 @@ __device__ __forceinline__ void rebuild_hist(Smem<CAP>& sm, u32 cnt) {
     const u32 tid = threadIdx.x;
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     __syncthreads();
-    for (u32 i = tid; i < cnt; i += WG) atomicAdd(&sm.hist[hidx(top_digit(sm.buf[i]))], 1u);
+    for (u32 base = 0; base < cnt; base += WG) {
+        const u32 i = base + tid;
+        hist_add(sm.hist, i < cnt ? top_digit(sm.buf[i]) : 0u, i < cnt);
+    }
     __syncthreads();
 }
 
@@ -976,6 +1007,239 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
     }
 }
 
+// ------------------------------------------------------------------ scan helpers
+// While scanning, buf[0, cbase) holds composites, counted in the histogram,
+// and the rest is split into one region of R entries per wave, where each
+// wave appends raw entries (element bits << 32 | column); wfill[w] counts
+// wave w's.  sync_regions moves them behind the composites, converting and
+// counting them with every lane busy, and returns the new count.  Entry j of
+// the regions' concatenation goes to cbase + j, at or below where it is,
+// and each batch is read before it is written, so nothing is overwritten
+// before it has been read.  A NaN sets sm.nan.  Call after a barrier that
+// follows every wave's last append and wfill store.  (Out of line: it runs
+// a few times per workgroup, and the scan keeps its registers.)
+template <class E, int WG, int CAP>
+__device__ __noinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
+    constexpr u32 kWaves = WG / kWave;
+    const u32 tid = threadIdx.x;
+    // Entry j of the concatenation lies at cbase + j plus the unused tails
+    // of the regions before its own: gap[q] = R - fill[q - 1] is added for
+    // every region start off[q] at or below j.
+    u32 off[kWaves], gap[kWaves], N = 0;
+#pragma unroll
+    for (u32 w = 0; w < kWaves; ++w) {
+        const u32 f = __builtin_amdgcn_readfirstlane(sm.wfill[w]);
+        off[w] = N;
+        gap[w] = w ? R - __builtin_amdgcn_readfirstlane(sm.wfill[w - 1]) : 0u;
+        N += f;
+    }
+    DSTK_PHASE(33);
+    bool nan = false;
+    constexpr u32 kB = 8;  // entries per thread and batch: one batch for most syncs
+    for (u32 base = 0; base < N; base += WG * kB) {
+        u64 e[kB];
+        u32 src[kB];
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) {
+            const u32 j = min(base + i * WG + tid, N - 1u);
+            u32 a = cbase + j;
+#pragma unroll
+            for (u32 q = 1; q < kWaves; ++q) a += j >= off[q] ? gap[q] : 0u;
+            src[i] = a;
+        }
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) e[i] = sm.buf[src[i]];
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) {
+            const u32 bits = (u32)(e[i] >> 32);
+            nan |= base + i * WG + tid < N && E::is_nan(bits);
+            e[i] = compose<E>(E::key(bits), (u32)e[i]);
+        }
+        __syncthreads();
+        DSTK_PHASE(34);
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) {
+            const u32 j = base + i * WG + tid;
+            if (j < N) sm.buf[cbase + j] = e[i];
+            hist_add(sm.hist, top_digit(e[i]), j < N);
+        }
+        __syncthreads();
+    }
+    if (nan) sm.nan = 1;  // benign race: every writer stores 1
+    DSTK_PHASE(35);
+    return cbase + N;
+}
+
+// After a sync of cnt composites: make room when the buffer is short of
+// `room` entries (room 0: when it is more than half full), then locate the
+// k-th counted entry and return the bound raised to its bin edge (and to
+// sm.L, which make_room may have raised); sm.count holds the new count.
+// Returns after a barrier.
+template <class E, int WG, int CAP>
+__device__ __noinline__ u64 raise_bound(Smem<CAP>& sm, u32 cnt, u32 room, u32 k, u64 L) {
+    if (room ? cnt > (u32)CAP - room : (cnt > (u32)CAP / 2 && cnt > k)) {
+        make_room<E, WG, CAP>(sm, cnt, k, room);
+    } else {
+        if (threadIdx.x == 0) sm.count = cnt;
+    }
+    block_locate<WG, CAP>(sm, k, 0u, false);
+    if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
+    if (sm.L > L) L = sm.L;
+    return L;
+}
+
+// ------------------------------------------------------------------ scan: admission
+// One segment's scan, per workgroup.  The state a wave carries from chunk to
+// chunk (all wave-uniform but `nan`).
+struct ScanState {
+    u64 L;      // admission bound: admit iff composite >= L
+    u32 cbase;  // buf[0, cbase) holds counted composites
+    u32 R;      // entries per wave region behind them
+    u32 wp;     // this wave's write pointer ...
+    u32 re;     // ... and region end
+    u32 par;    // slot of sm.pflag used by the next check
+    u32 exact;  // also test survivors against the composite bound
+    u32 nan;    // per lane: a NaN met by the exact test
+};
+// What a scan reads but never changes.
+struct ScanCtx {
+    __amdgpu_buffer_rsrc_t rsrc;  // the segment; offset (vi - v0) * 16
+    int v0, v1;                   // vectors [v0, v1) of the row
+    u32 n, k;
+};
+
+template <int WG, int CAP>
+__device__ __forceinline__ void assign_regions(ScanState& st, u32 cnt) {
+    constexpr u32 kWaves = WG / kWave;
+    st.cbase = cnt;
+    st.R = ((u32)CAP - cnt) / kWaves;
+    st.wp = cnt + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * st.R;
+    st.re = st.wp + st.R;
+}
+
+// Appends the survivors of one tile (vector vb + thread of the row) to the
+// wave's region: one ballot per element slot gives them as scalar masks,
+// so every branch is on a scalar, and every lane writes, with no branch or
+// exec mask per slot: a survivor to its place behind the write pointer, any
+// other lane to its own word of a scratch row.  In exact mode the survivors
+// are also tested against the composite bound, so long runs of values equal
+// to the bound's value cannot refill the buffer.  Returns false (nothing
+// appended) when they do not fit.
+template <class E, int WG, int CAP>
+__device__ __forceinline__ bool append_tile(Smem<CAP>& sm, const ScanCtx& cx, ScanState& st, const PreFilter<E>& pf,
+                                            const u32x4& x, int vb) {
+    constexpr int P = E::kPerVec;
+    constexpr int kTileVecs = WG;
+    const u32 dw[4] = {x[0], x[1], x[2], x[3]};
+    const u32 vi = (u32)(vb + (int)threadIdx.x);
+    u64 m[P];
+    u64 any = 0;
+    static_for<P>([&](auto S_) {
+        constexpr int s = decltype(S_)::value;
+        m[s] = __ballot(pass_slot<s>(pf, dw));
+        any |= m[s];
+    });
+    if (any == 0) return true;
+    if (!(vb + kTileVecs <= cx.v1 && (u32)(vb + kTileVecs) * P <= cx.n)) {
+        // the tile runs past the valid columns
+        static_for<P>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            m[s] &= __ballot((int)vi < cx.v1 && vi * P + s < cx.n);
+        });
+    }
+    if (st.exact) {
+        static_for<P>([&](auto S_) {
+            constexpr int s = decltype(S_)::value;
+            if (m[s]) {
+                // (a NaN passes the pre-filter; note it before the exact test)
+                st.nan |= (((m[s] >> lane_id()) & 1u) && nan_slot<s>(E{}, dw)) ? 1u : 0u;
+                m[s] &= __ballot(compose<E>(E::key(slot_bits<s>(E{}, dw)), vi * P + s) >= st.L);
+            }
+        });
+    }
+    u32 tot = 0;
+    static_for<P>([&](auto S_) { tot += (u32)__popcll(m[decltype(S_)::value]); });
+    if (st.wp + tot > st.re) return false;
+    // (the element bits go into the store's register pair as a fresh copy,
+    // so the loaded vectors stay where the loads put them)
+    u64* const trash = &sm.trash[lane_id()];
+    static_for<P>([&](auto S_) {
+        constexpr int s = decltype(S_)::value;
+        u64* const dst = __builtin_amdgcn_inverse_ballot_w64(m[s]) ? &sm.buf[mbcnt_from(m[s], st.wp)] : trash;
+        *dst = ((u64)fresh_copy(slot_bits<s>(E{}, dw)) << 32) | (vi * P + s);
+        st.wp += (u32)__popcll(m[s]);
+    });
+    return true;
+}
+
+// Appends tiles from..NV-1 of a chunk (constant register indices); returns
+// the first tile that did not fit, or NV.
+template <class E, int WG, int NV, int CAP>
+__device__ __forceinline__ u32 append_chunk(Smem<CAP>& sm, const ScanCtx& cx, ScanState& st, const PreFilter<E>& pf,
+                                            const u32x4 (&v)[NV], const int (&vb)[NV], u32 from) {
+    u32 stop = (u32)NV;
+    static_for<NV>([&](auto I_) {
+        constexpr int i = decltype(I_)::value;
+        if (stop == (u32)NV && (u32)i >= from && !append_tile<E, WG, CAP>(sm, cx, st, pf, v[i], vb[i]))
+            stop = (u32)i;
+    });
+    return stop;
+}
+
+// "Is any wave left with tiles?" in one barrier: slot par collects the
+// answer; the other slot, last read before an earlier barrier, is cleared
+// for the next check.  The barrier also follows every wave's last append
+// and fill note, as a sync needs.
+template <int WG, int CAP>
+__device__ __forceinline__ bool check_pending(Smem<CAP>& sm, ScanState& st, bool pending) {
+    constexpr u32 kWaves = WG / kWave;
+    const u32 wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (lane_id() == 0) {
+        if (pending) atomicOr(&sm.pflag[st.par], 1u);
+        sm.wfill[wave] = st.wp - (st.cbase + wave * st.R);
+    }
+    if (threadIdx.x == 0) sm.pflag[st.par ^ 1u] = 0;
+    __syncthreads();
+    const bool again = sm.pflag[st.par] != 0;
+    st.par ^= 1u;
+    (void)kWaves;
+    return again;
+}
+
+// The rare step after a chunk: a region filled up (again), or a scheduled
+// raise.  Sync; make room if the buffer is short of a whole tile of the
+// workgroup, raise the bound; with tiles left, reload them (from the cache)
+// and append them, and repeat.  With that much room every region holds one
+// wave's tile, so each round appends at least one tile of every waiting
+// wave, and at most NV + 1 rounds are taken.  Out of line: the common path
+// keeps its registers.
+template <class E, int WG, int NV, int CAP>
+__device__ __noinline__ ScanState rare_rounds(Smem<CAP>& sm, ScanCtx cx, ScanState st, VecBases<NV> vb, u32 rtile,
+                                              bool again) {
+    constexpr u32 kTileElems = WG * E::kPerVec;
+    for (u32 round = 0;; ++round) {
+        if (round > (u32)NV) {  // unreachable: the room argument above
+            st.nan = 1;  // reported as an invalid result, never silently
+            break;
+        }
+        const u32 cnt = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
+        st.L = raise_bound<E, WG, CAP>(sm, cnt, again ? kTileElems : 0u, cx.k, st.L);
+        st.exact |= again ? 1u : 0u;
+        assign_regions<WG, CAP>(st, __builtin_amdgcn_readfirstlane(sm.count));
+        if (!again) break;
+        PreFilter<E> pf;
+        pf.set(st.L);
+        u32x4 w[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            w[i] = __builtin_amdgcn_raw_buffer_load_b128(cx.rsrc, (u32)(vb.b[i] + (int)threadIdx.x - cx.v0) * 16u, 0, 0);
+        rtile = append_chunk<E, WG, NV, CAP>(sm, cx, st, pf, w, vb.b, rtile);
+        again = check_pending<WG, CAP>(sm, st, rtile < (u32)NV);
+        if (!again) break;
+    }
+    return st;
+}
+
 // ------------------------------------------------------------------ kernel
 struct Params {
     const uint8_t* in;
@@ -1023,12 +1287,12 @@ template <class E, int VPT, int WG>
 struct Slot {
     static constexpr int kSlots = VPT * E::kPerVec;
     static constexpr int kPerDword = E::kKeyBits == 16 ? 2 : 1;
-    __device__ static __forceinline__ void get(const uint4 (&v)[VPT], int s, int vb, u32 tid, int v1, u32 n,
+    __device__ static __forceinline__ void get(const u32x4 (&v)[VPT], int s, int vb, u32 tid, int v1, u32 n,
                                                u32& bits, u32& col, bool& valid) {
         const int j = s / E::kPerVec;
         const int w = (s % E::kPerVec) / kPerDword;
         const int hh = s % kPerDword;
-        const u32 d = w == 0 ? v[j].x : w == 1 ? v[j].y : w == 2 ? v[j].z : v[j].w;
+        const u32 d = v[j][w];
         bits = kPerDword == 2 ? ((d >> (16 * hh)) & 0xFFFFu) : d;
         const int vi = vb + j * WG + (int)tid;
         col = (u32)vi * E::kPerVec + (u32)(w * kPerDword + hh);
@@ -1145,9 +1409,8 @@ void topk_rows(Params p) {
     // returns zeros past the segment's end instead of faulting.
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(row_in + (int64_t)v0 * 16), (short)0, (int)((u32)(v1 - v0) * 16u), kBufferWord3);
-    auto load_vec = [&](int vi) -> uint4 {  // vi: absolute vector index in the row
-        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(vi - v0) * 16u, 0, 0);
-        return uint4{r[0], r[1], r[2], r[3]};
+    auto load_vec = [&](int vi) -> u32x4 {  // vi: absolute vector index in the row
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(vi - v0) * 16u, 0, 0);
     };
     const u32 ntiles = (u32)((v1 - v0 + kTileVecs - 1) / kTileVecs);
 
@@ -1174,149 +1437,27 @@ void topk_rows(Params p) {
     DSTK_PHASE(0);
 
     PreFilter<E> pf;
-    u64 L = 0;
-    pf.set(L);
+    pf.set(0ull);
     __syncthreads();
 
     u32 pr = b;  // permuted index of the next tile to request
-    u32 par = 0;  // slot of sm.pflag used by the next overflow check
-    constexpr int kSeed = NV < 2 ? NV : 2;  // tiles counted to seed the bound
-    static_assert(CAP >= kSeed * kTileElems, "the seed tiles must fit an empty buffer");
+    // Tiles counted to seed the bound: the whole first chunk, as far as an
+    // empty buffer holds it.  A tighter seed pays for itself: every later
+    // tile is filtered against it, and a raise costs a sync and a locate.
+    constexpr int kSeed = NV < CAP / kTileElems ? NV : CAP / kTileElems;
+    static_assert(kSeed >= 1, "the seed tiles must fit an empty buffer");
 
-    // ---- buffer layout while scanning.  buf[0, cbase) holds composites,
-    // counted in the histogram.  The free part is split into one region of
-    // R entries per wave; a wave appends raw entries (element bits << 32 |
+    // ---- buffer layout while scanning: buf[0, cbase) holds composites,
+    // counted in the histogram; the free part is split into one region of R
+    // entries per wave.  A wave appends raw entries (element bits << 32 |
     // column) to its own region behind a scalar write pointer, with no
-    // atomics and no barrier.  A sync moves the regions' entries behind the
+    // atomics and no barrier; a sync moves the regions' entries behind the
     // composites, converting and counting them with every lane busy.
-    constexpr u32 kWaves = WG / kWave;
-    const u32 wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
-    u32 cbase = 0, R = (u32)CAP / kWaves;  // wave-uniform
-    u32 wp = wave_u * R, re = wp + R;       // this wave's write pointer and region end
-    auto assign_regions = [&](u32 cnt) __attribute__((always_inline)) {
-        cbase = cnt;
-        R = ((u32)CAP - cnt) / kWaves;
-        wp = cnt + wave_u * R;
-        re = wp + R;
-    };
-    // Call before the barrier that precedes a sync.
-    auto note_fill = [&]() __attribute__((always_inline)) {
-        if (lane_id() == 0) sm.wfill[wave_u] = wp - (cbase + wave_u * R);
-    };
-    bool saw_nan = false;  // per lane
-    // Move, convert and count; returns the new number of composites.  Entry j
-    // of the regions' concatenation goes to cbase + j, at or below where it
-    // is, and every batch is read before it is written, so no entry is
-    // overwritten before it has been read.
-    auto sync_buffer = [&]() __attribute__((always_inline)) -> u32 {
-        u32 fill[kWaves], off[kWaves], N = 0;
-#pragma unroll
-        for (u32 w = 0; w < kWaves; ++w) {
-            fill[w] = __builtin_amdgcn_readfirstlane(sm.wfill[w]);
-            off[w] = N;
-            N += fill[w];
-        }
-        constexpr u32 kB = 4;
-        for (u32 base = 0; base < N; base += WG * kB) {
-            u64 e[kB];
-#pragma unroll
-            for (u32 i = 0; i < kB; ++i) {
-                const u32 j = base + i * WG + tid;
-                e[i] = 0;
-                if (j < N) {
-                    u32 w = 0;
-#pragma unroll
-                    for (u32 q = 1; q < kWaves; ++q) w = j >= off[q] ? q : w;
-                    const u64 raw = sm.buf[cbase + w * R + (j - off[w])];
-                    const u32 bits = (u32)(raw >> 32);
-                    saw_nan |= E::is_nan(bits);
-                    e[i] = compose<E>(E::key(bits), (u32)raw);
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (u32 i = 0; i < kB; ++i) {
-                const u32 j = base + i * WG + tid;
-                if (j < N) {
-                    sm.buf[cbase + j] = e[i];
-                    atomicAdd(&sm.hist[hidx(top_digit(e[i]))], 1u);
-                }
-            }
-            __syncthreads();
-        }
-        return cbase + N;
-    };
+    const ScanCtx cx{rsrc, v0, v1, n, k};
+    ScanState st{};
+    assign_regions<WG, CAP>(st, 0u);
 
-    // ---- admission.  One ballot per element slot gives the wave's
-    // pre-filter survivors as scalar masks, so every branch is on a scalar.
-    // In exact mode (entered once the buffer has overflowed) the survivors
-    // are also tested against the composite bound, so long runs of values
-    // equal to the bound's value cannot refill the buffer.
-    bool exact = false;        // wave-uniform
-    constexpr int P = E::kPerVec;
-    // Appends one tile's survivors; false (nothing appended) when they do not
-    // fit in the wave's region.
-    auto append_tile = [&](const uint4& x, const int vb) __attribute__((always_inline)) -> bool {
-        const u32 dw[4] = {x.x, x.y, x.z, x.w};
-        const u32 vi = (u32)(vb + (int)tid);
-        u64 m[P];
-        u64 any = 0;
-        static_for<P>([&](auto S_) {
-            constexpr int s = decltype(S_)::value;
-            m[s] = __ballot(pass_slot<s>(pf, dw));
-            any |= m[s];
-        });
-        if (any == 0) return true;
-        if (!(vb + kTileVecs <= v1 && (u32)(vb + kTileVecs) * P <= n)) {
-            // the tile runs past the valid columns
-            static_for<P>([&](auto S_) {
-                constexpr int s = decltype(S_)::value;
-                m[s] &= __ballot((int)vi < v1 && vi * P + s < n);
-            });
-        }
-        if (exact) {
-            static_for<P>([&](auto S_) {
-                constexpr int s = decltype(S_)::value;
-                if (m[s]) {
-                    // (a NaN passes the pre-filter; note it before the exact test)
-                    saw_nan |= ((m[s] >> lane_id()) & 1u) && nan_slot<s>(E{}, dw);
-                    m[s] &= __ballot(compose<E>(E::key(slot_bits<s>(E{}, dw)), vi * P + s) >= L);
-                }
-            });
-        }
-        u32 tot = 0;
-        static_for<P>([&](auto S_) { tot += (u32)__popcll(m[decltype(S_)::value]); });
-        if (wp + tot > re) return false;
-        // (no branch per slot: with an empty mask the writes are no-ops)
-        static_for<P>([&](auto S_) {
-            constexpr int s = decltype(S_)::value;
-            if (__builtin_amdgcn_inverse_ballot_w64(m[s]))
-                sm.buf[mbcnt_from(m[s], wp)] = ((u64)slot_bits<s>(E{}, dw) << 32) | (vi * P + s);
-            wp += (u32)__popcll(m[s]);
-        });
-        return true;
-    };
-    // Appends tiles from..NV-1 of a chunk (constant register indices);
-    // returns the first tile that did not fit, or NV.
-    auto append_chunk = [&](const uint4 (&v)[NV], const int (&vb)[NV], u32 from) __attribute__((always_inline)) -> u32 {
-        u32 stop = (u32)NV;
-        static_for<NV>([&](auto I_) {
-            constexpr int i = decltype(I_)::value;
-            if (stop == (u32)NV && (u32)i >= from && !append_tile(v[i], vb[i])) stop = (u32)i;
-        });
-        return stop;
-    };
-
-    // Chunks of NV tiles, double-buffered: the loads of chunk c+1 are in
-    // flight while chunk c is processed.  Processing a chunk: a short
-    // unrolled pass waits for each tile in request order and notes which
-    // tiles have elements past the pre-filter; once the chunk has arrived,
-    // one rolled loop (the same code for every tile, so it is fetched once)
-    // appends their admitted elements.  No workgroup barrier is taken while
-    // appending: waves run independently and hide each other's load
-    // latency.  A wave whose entries do not fit records the tile; phase B
-    // makes room and filters those tiles again.
-    auto issue = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
+    auto issue = [&](u32 t0, u32x4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             vb[i] = t0 + (u32)i < ntiles ? v0 + (int)pr * kTileVecs : v1;
@@ -1329,78 +1470,66 @@ void topk_rows(Params p) {
     // Seed: count every element of the first kSeed tiles and take the bin
     // edge of the k-th counted as the bound; those tiles are then appended
     // like the others.
-    auto seed = [&](const uint4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
+    auto seed = [&](const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
+        auto count = [&](auto agg_tag) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kSeed; ++i) {
-            const uint4 xs[1] = {v[i]};
+            for (int i = 0; i < kSeed; ++i) {
+                const u32x4 xs[1] = {v[i]};
 #pragma unroll
-            for (int s = 0; s < SL::kSlots; ++s) {
-                u32 bits, col;
-                bool valid;
-                SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
-                if (valid) atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(bits), col)))], 1u);
+                for (int s = 0; s < SL::kSlots; ++s) {
+                    u32 bits, col;
+                    bool valid;
+                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                    const u32 d = top_digit(compose<E>(E::key(bits), col));
+                    if constexpr (decltype(agg_tag)::value)
+                        hist_add(sm.hist, d, valid);
+                    else if (valid)
+                        atomicAdd(&sm.hist[hidx(d)], 1u);
+                }
             }
+        };
+        // Runs of equal values (padding, quantized scores) put whole waves
+        // in one bin: then count by wave where the lanes agree.  The wave's
+        // first elements decide, for its whole seed.
+        u32 b0, c0;
+        bool ok0;
+        {
+            const u32x4 xs[1] = {v[0]};
+            SL::get(xs, 0, vb[0], tid, v1, n, b0, c0, ok0);
         }
+        const u32 d0 = top_digit(compose<E>(E::key(b0), c0));
+        if (__ballot(ok0) == ~0ull && __ballot(d0 != __builtin_amdgcn_readfirstlane(d0)) == 0)
+            count(std::true_type{});
+        else
+            count(std::false_type{});
         DSTK_PHASE(19);
         __syncthreads();
         // the locate also clears the histogram: from here on it counts
         // exactly the synced entries
         block_locate<WG, CAP>(sm, k, 0u, true);
-        if (sm.loc_c[0] > 0) L = digit_floor(sm.loc_digit[0]);
-        pf.set(L);
+        if (sm.loc_c[0] > 0) st.L = digit_floor(sm.loc_digit[0]);
+        pf.set(st.L);
         DSTK_PHASE(7);
     };
-    // Append a chunk.  When a region is full (rare): sync, make room if the
-    // buffer is short of a whole tile of the workgroup, raise the bound and
-    // resume.  With that much room every region holds one wave's tile, so
-    // each round appends at least one tile of every waiting wave and at most
-    // NV + 1 rounds are taken.  After chunks 0, 1, 3, 7, 15, ... (a fixed
-    // schedule, so every wave takes the same barriers; the bound tightens
-    // roughly as the number of elements seen doubles) the same step syncs
-    // and raises the bound without a resume.
-    auto process = [&](u32 t0, uint4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
+    // Append a chunk, then check.  After chunks 7, 15, 31, ... (a fixed
+    // schedule, so every wave takes the same barriers; on long segments the
+    // bound then tightens as the number of elements seen doubles) the rare
+    // step syncs and raises the bound.  Shorter segments keep the seed's
+    // bound: a raise there costs more than the appends it saves, and a full
+    // region raises the bound anyway.
+    auto process = [&](u32 t0, const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
         if (t0 == 2 * NV) DSTK_PHASE(29);
         const u32 c = t0 / NV;
-        const bool raise = t0 + NV < ntiles && ((c + 1) & c) == 0;
-        u32 rtile = 0;  // wave-uniform: first tile not appended yet, or NV
-        for (u32 round = 0;; ++round) {
-            // (keeps the exact-mode and resume work inside the rounds rather
-            // than hoisted in front of the common first round)
+        const bool raise = t0 + NV < ntiles && c >= 7 && ((c + 1) & c) == 0;
+        const u32 rtile = append_chunk<E, WG, NV, CAP>(sm, cx, st, pf, v, vb, 0u);
+        if (t0 == 2 * NV) DSTK_PHASE(30);
+        const bool again = check_pending<WG, CAP>(sm, st, rtile < (u32)NV);
+        if (again || raise) {
+            VecBases<NV> bases;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                opaque(v[i]);
-                opaque_s(vb[i]);
-            }
-            if (rtile < (u32)NV) rtile = append_chunk(v, vb, rtile);
-            if (t0 == 2 * NV && round == 0) DSTK_PHASE(30);
-            // "any wave left over?" in one barrier: slot `par` collects the
-            // answer; the other slot, last read before an earlier barrier,
-            // is cleared for the next check.  The barrier also follows every
-            // wave's last append and fill note, as a sync needs.
-            if (lane_id() == 0 && rtile < (u32)NV) atomicOr(&sm.pflag[par], 1u);
-            if (tid == 0) sm.pflag[par ^ 1u] = 0;
-            note_fill();
-            __syncthreads();
-            const bool again = sm.pflag[par] != 0;
-            par ^= 1u;
-            if (!again && !(raise && round == 0)) break;
-            if (round > (u32)NV) {  // unreachable: the room argument above
-                saw_nan = true;  // reported as an invalid result, never silently
-                break;
-            }
-            const u32 cnt = sync_buffer();
-            if (again ? cnt > (u32)(CAP - kTileElems) : (cnt > (u32)CAP / 2 && cnt > k)) {
-                make_room<E, WG, CAP>(sm, cnt, k, again ? (u32)kTileElems : 0u);
-            } else {
-                if (tid == 0) sm.count = cnt;
-            }
-            exact = exact || again;
-            block_locate<WG, CAP>(sm, k, 0u, false);
-            if (sm.loc_c[0] > 0 && digit_floor(sm.loc_digit[0]) > L) L = digit_floor(sm.loc_digit[0]);
-            if (sm.L > L) L = sm.L;
-            pf.set(L);
-            assign_regions(__builtin_amdgcn_readfirstlane(sm.count));
-            if (!again) break;
+            for (int i = 0; i < NV; ++i) bases.b[i] = vb[i];
+            st = rare_rounds<E, WG, NV, CAP>(sm, cx, st, bases, rtile, again);
+            pf.set(st.L);
         }
         if (t0 == 2 * NV) DSTK_PHASE(31);
         DSTK_PHASE(25 + (c < 6u ? c : 6u));
@@ -1411,26 +1540,33 @@ void topk_rows(Params p) {
         // segment's end (such tiles are range-checked buffer loads that
         // return zeros and touch no memory), so every path has the same loads
         // in flight and each tile waits only for its own load.
-        uint4 va[NV], vc[NV];
+        // The loop is entered, and re-entered, with only vc's loads in
+        // flight, so the wait before each tile covers exactly that tile's
+        // load.
+        u32x4 va[NV], vc[NV];
         int vba[NV], vbc[NV];
         issue(0, va, vba);
         issue(NV, vc, vbc);
         seed(va, vba);
-        for (u32 t0 = 0;; t0 += 2 * NV) {
-            process(t0, va, vba);
-            if (t0 + NV >= ntiles) break;
-            issue(t0 + 2 * NV, va, vba);
-            process(t0 + NV, vc, vbc);
-            if (t0 + 2 * NV >= ntiles) break;
-            issue(t0 + 3 * NV, vc, vbc);
+        process(0, va, vba);
+        if ((u32)NV < ntiles) {
+            for (u32 t0 = NV;; t0 += 2 * NV) {
+                issue(t0 + NV, va, vba);
+                process(t0, vc, vbc);
+                if (t0 + NV >= ntiles) break;
+                issue(t0 + 2 * NV, vc, vbc);
+                process(t0 + NV, va, vba);
+                if (t0 + 2 * NV >= ntiles) break;
+            }
         }
     }
     {
         // the last check's barrier follows every wave's last append
-        const u32 cnt = sync_buffer();
+        const u32 cnt = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
         if (tid == 0) sm.count = cnt;
     }
-    if (saw_nan) sm.nan = 1;  // benign race: every writer stores 1
+    if (st.nan) sm.nan = 1;  // benign race: every writer stores 1
+    u64 L = st.L;
     if (tid == 0) sm.L = L;
     DSTK_PHASE(1);
     __syncthreads();
