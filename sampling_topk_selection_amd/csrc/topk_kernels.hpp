@@ -1070,6 +1070,93 @@ __device__ __noinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
     return cbase + N;
 }
 
+// Where entry j of the scan's buffer lies when the regions have not been
+// moved together: below cbase at j, past it behind the unused tails of the
+// regions before its own (see sync_regions).
+template <int WG>
+struct RegionMap {
+    static constexpr u32 kWaves = WG / kWave;
+    u32 cbase, total;
+    u32 off[kWaves], gap[kWaves];
+    template <int CAP>
+    __device__ __forceinline__ RegionMap(const Smem<CAP>& sm, u32 cb, u32 R) : cbase(cb) {
+        u32 N = 0;
+#pragma unroll
+        for (u32 w = 0; w < kWaves; ++w) {
+            off[w] = N;
+            gap[w] = w ? R - __builtin_amdgcn_readfirstlane(sm.wfill[w - 1]) : 0u;
+            N += __builtin_amdgcn_readfirstlane(sm.wfill[w]);
+        }
+        total = cb + N;
+    }
+    __device__ __forceinline__ u32 addr(u32 j) const {
+        if (j < cbase) return j;
+        const u32 r = j - cbase;
+        u32 a = j;
+#pragma unroll
+        for (u32 q = 1; q < kWaves; ++q) a += r >= off[q] ? gap[q] : 0u;
+        return a;
+    }
+};
+
+// Moves the (converted, counted) entries of the regions together behind
+// cbase, in batches each read before it is written (see sync_regions);
+// returns the count.  Returns after a barrier.
+template <int WG, int CAP>
+__device__ __forceinline__ u32 move_regions(Smem<CAP>& sm, const RegionMap<WG>& map) {
+    const u32 tid = threadIdx.x;
+    constexpr u32 kB = 8;
+    for (u32 base = map.cbase; base < map.total; base += WG * kB) {
+        u64 e[kB];
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) {
+            const u32 j = base + i * WG + tid;
+            e[i] = j < map.total ? sm.buf[map.addr(j)] : 0ull;
+        }
+        __syncthreads();
+#pragma unroll
+        for (u32 i = 0; i < kB; ++i) {
+            const u32 j = base + i * WG + tid;
+            if (j < map.total) sm.buf[j] = e[i];
+        }
+        __syncthreads();
+    }
+    return map.total;
+}
+
+// Converts the regions' raw entries to composites where they lie and counts
+// them (the split-row end of scan, which publishes from there; the regions
+// are not moved together).  Each wave converts its own region.  A NaN sets
+// sm.nan.  Call after a barrier that follows every wave's last append and
+// wfill store; returns after a barrier.
+template <class E, int WG, int CAP>
+__device__ __noinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
+    const u32 wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const u32 fill = __builtin_amdgcn_readfirstlane(sm.wfill[wave]);
+    const u32 rb = cbase + wave * R;
+    bool nan = false;
+    constexpr u32 kU = 4;  // entries in flight per lane
+    for (u32 i0 = 0; i0 < fill; i0 += kU * kWave) {
+        u64 e[kU];
+#pragma unroll
+        for (u32 u = 0; u < kU; ++u) {
+            const u32 i = i0 + u * kWave + lane_id();
+            e[u] = i < fill ? sm.buf[rb + i] : 0ull;
+        }
+#pragma unroll
+        for (u32 u = 0; u < kU; ++u) {
+            const u32 i = i0 + u * kWave + lane_id();
+            const u32 bits = (u32)(e[u] >> 32);
+            nan |= i < fill && E::is_nan(bits);
+            e[u] = compose<E>(E::key(bits), (u32)e[u]);
+            if (i < fill) sm.buf[rb + i] = e[u];
+            hist_add(sm.hist, top_digit(e[u]), i < fill);
+        }
+    }
+    if (nan) sm.nan = 1;  // benign race: every writer stores 1
+    __syncthreads();
+}
+
 // After a sync of cnt composites: make room when the buffer is short of
 // `room` entries (room 0: when it is more than half full), then locate the
 // k-th counted entry and return the bound raised to its bin edge (and to
@@ -1560,10 +1647,13 @@ void topk_rows(Params p) {
             }
         }
     }
-    {
-        // the last check's barrier follows every wave's last append
-        const u32 cnt = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
-        if (tid == 0) sm.count = cnt;
+    // (the last check's barrier follows every wave's last append)
+    if (p.segs == 1) {
+        const u32 c = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
+        if (tid == 0) sm.count = c;
+    } else {
+        // a split row publishes from where the entries lie
+        convert_regions<E, WG, CAP>(sm, st.cbase, st.R);
     }
     if (st.nan) sm.nan = 1;  // benign race: every writer stores 1
     u64 L = st.L;
@@ -1600,8 +1690,14 @@ void topk_rows(Params p) {
         u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
         u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
         u64 bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
+        const RegionMap<WG> map(sm, st.cbase, st.R);
+        bool moved = false;  // the regions have been moved together
         if (live > (u32)p.pub_cap) {
-            // too many to publish: reduce this segment exactly to k first
+            // too many to publish: move the entries together (already
+            // counted: the move alone), then reduce exactly to k
+            __syncthreads();  // everyone has built the map from wfill
+            cnt = move_regions<WG, CAP>(sm, map);
+            moved = true;
             cnt = reduce_to_k<WG, CAP>(sm, cnt, k, q, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0]);
             if (sm.kth > L) L = sm.kth;
             dl = sm.loc_digit[0];
@@ -1640,8 +1736,9 @@ void topk_rows(Params p) {
         }
         __syncthreads();
         u64* cand = p.ws_cand + (u64)slot * (u32)p.pub_cap;
-        for (u32 i = tid; i < cnt; i += WG) {
-            const u64 e = sm.buf[i];
+        const u32 total = moved ? cnt : map.total;
+        for (u32 i = tid; i < total; i += WG) {
+            const u64 e = sm.buf[moved ? i : map.addr(i)];
             const u32 d = top_digit(e);
             if (live > 0 && d >= dl) {
                 const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
