@@ -191,7 +191,7 @@ struct Smem {
     u32 pflag[2];        // scan: "some wave has a tile left over", two slots
     u32 wfill[16];       // scan: raw entries each wave has appended since the last sync
     u32 lwsum[16];       // block_locate: per-wave bin totals
-    u32 lwfirst[16];     // block_locate: per-wave first thread with a non-empty bin, or 64
+    u32 lwfirst[16];     // block_locate: per-wave highest non-empty bin (waves with any)
     u64 trash[64];       // scan: written by the lanes that append nothing
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
 #ifdef DSTK_PROBE_SLOTS
@@ -774,8 +774,8 @@ __device__ __forceinline__ u64 low_mask(int b) { return b >= 64 ? ~0ull : ((1ull
 // higher bins, and the thread whose bins hold rank r writes the result.
 // Call from every thread; returns after a barrier, with the results visible
 // to all.  With `zero` the histogram is cleared on the way.
-template <int WG, int CAP>
-__device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero) {
+template <int WG, int CAP, bool kPub = false>
+__device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero, u32* dir = nullptr) {
     constexpr u32 kPer = kBins / WG;
     constexpr u32 kW = WG / kWave;
     static_assert(kPer * WG == kBins && kW <= 16, "bins per thread");
@@ -792,7 +792,14 @@ __device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool
     const u32 incl = wave_incl_scan(s);
     const u64 nz = __ballot(s != 0);
     if (l == kWave - 1) sm.lwsum[wave] = incl;
-    if (l == 0) sm.lwfirst[wave] = nz ? (u32)__builtin_ctzll(nz) : (u32)kWave;
+    if (nz && l == (u32)__builtin_ctzll(nz)) {
+        // this wave's highest non-empty bin
+        u32 d = 0;
+#pragma unroll
+        for (int j = (int)kPer - 1; j >= 0; --j)
+            if (c[j]) d = kBins - 1u - (tid * kPer + (u32)j);
+        sm.lwfirst[wave] = d;
+    }
     __syncthreads();
     u32 off = 0, tot = 0, fw = kW;
 #pragma unroll
@@ -802,6 +809,7 @@ __device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool
         tot += v;
         fw = (fw == kW && v != 0) ? w : fw;
     }
+    const u32 dh = fw == kW ? 0u : sm.lwfirst[fw];
     const u32 excl = off + incl - s;  // entries in bins above this thread's
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -828,15 +836,25 @@ __device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool
             }
         }
     }
-    if (tid == 0) sm.loc_total = tot;
-    if (fw == kW) {
-        if (tid == 0) sm.loc_dhi = 0;
-    } else if (wave == fw && l == sm.lwfirst[fw]) {
-        u32 d = 0;
+    if (tid == 0) {
+        sm.loc_total = tot;
+        sm.loc_dhi = dh;
+    }
+    if constexpr (kPub) {
+        // Publishing: for every bin from the highest non-empty one down to
+        // the bin of the r0-th entry, the directory entry (entries at or
+        // above the bin) and, over the histogram, the bin's first slot in
+        // the descending list.
+        u32 above = excl;
 #pragma unroll
-        for (int j = (int)kPer - 1; j >= 0; --j)
-            if (c[j]) d = kBins - 1u - (tid * kPer + (u32)j);
-        sm.loc_dhi = d;
+        for (u32 j = 0; j < kPer; ++j) {
+            const u32 d = kBins - 1u - (tid * kPer + j);
+            if (d <= dh && above < r0) {
+                sm.hist[hidx(d)] = above;
+                st_agent(&dir[dh - d], above + c[j]);
+            }
+            above += c[j];
+        }
     }
     __syncthreads();
 }
@@ -918,8 +936,9 @@ __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k
 // Reduce buf[0, cnt) exactly to its k largest (b1/r1/c1 locate the k-th in
 // the histogram), rebuild the histogram and locate ranks k and q again.
 // Returns the new count; sm.kth gets the k-th entry.
-template <int WG, int CAP>
-__device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u32 b1, u32 r1, u32 c1) {
+template <int WG, int CAP, bool kPub = false>
+__device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u32 b1, u32 r1, u32 c1,
+                                        u32* dir = nullptr) {
     const u32 tid = threadIdx.x;
     __syncthreads();
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
@@ -929,7 +948,7 @@ __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u3
     cnt = keep_at_least<WG, CAP>(sm, 0, cnt, T);
     if (tid == 0) sm.kth = T;
     rebuild_hist<WG, CAP>(sm, cnt);
-    block_locate<WG, CAP>(sm, k, q, false);
+    block_locate<WG, CAP, kPub>(sm, k, q, false, dir);
     return cnt;
 }
 
@@ -1685,7 +1704,9 @@ void topk_rows(Params p) {
         // q = ceil(k / S): with every segment holding q entries at or above
         // its q-bound, the smallest q-bound over the row is a valid bound too
         const u32 q = (k + S - 1) / S;
-        block_locate<WG, CAP>(sm, k, q, false);
+        u32* dir = p.ws_dir + (u64)slot * kBins;
+        // locate, directory and placement offsets in one pass over the bins
+        block_locate<WG, CAP, true>(sm, k, q, false, dir);
         DSTK_PHASE(11);
         u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
         u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
@@ -1698,7 +1719,8 @@ void topk_rows(Params p) {
             __syncthreads();  // everyone has built the map from wfill
             cnt = move_regions<WG, CAP>(sm, map);
             moved = true;
-            cnt = reduce_to_k<WG, CAP>(sm, cnt, k, q, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0]);
+            // (the histogram is counted again; the directory is rewritten)
+            cnt = reduce_to_k<WG, CAP, true>(sm, cnt, k, q, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], dir);
             if (sm.kth > L) L = sm.kth;
             dl = sm.loc_digit[0];
             live = sm.loc_above[0] + sm.loc_c[0];
@@ -1706,35 +1728,13 @@ void topk_rows(Params p) {
         }
         DSTK_PHASE(10);
         const u32 dh = sm.loc_dhi;
-        u32* dir = p.ws_dir + (u64)slot * kBins;
-        if (wave == 0) {
-            // placement offsets (entries in higher bins) for bins in [dl, dh],
-            // written over the histogram, and the directory; 64 bins a step,
-            // lane i taking bin dh - step - i (descending)
-            const u32 l = lane_id();
-            if (live > 0) {
-                u32 carry = 0;
-                for (u32 b0 = 0; b0 <= dh - dl; b0 += kWave) {
-                    const u32 j = b0 + l;
-                    const bool in = j <= dh - dl;
-                    const u32 c = in ? sm.hist[hidx(dh - j)] : 0u;
-                    const u32 ci = wave_incl_scan(c);
-                    if (in) {
-                        sm.hist[hidx(dh - j)] = carry + ci - c;
-                        st_agent(&dir[j], carry + ci);
-                    }
-                    carry += __builtin_amdgcn_readlane(ci, 63);
-                }
-            }
-            if (l == 0) {
-                u64* meta = p.ws_meta + (u64)slot * 4;
-                st_agent(&meta[0], (u64)live | ((u64)dl << 32));
-                st_agent(&meta[1], (u64)(live ? dh : 0u));
-                st_agent(&meta[2], L);
-                st_agent(&meta[3], bq);
-            }
+        if (tid == 0) {
+            u64* meta = p.ws_meta + (u64)slot * 4;
+            st_agent(&meta[0], (u64)live | ((u64)dl << 32));
+            st_agent(&meta[1], (u64)(live ? dh : 0u));
+            st_agent(&meta[2], L);
+            st_agent(&meta[3], bq);
         }
-        __syncthreads();
         u64* cand = p.ws_cand + (u64)slot * (u32)p.pub_cap;
         const u32 total = moved ? cnt : map.total;
         for (u32 i = tid; i < total; i += WG) {
