@@ -682,6 +682,67 @@ __device__ __noinline__ void final_select(Smem<CAP>& sm, u32 cnt, u32 k) {
 }
 
 // ------------------------------------------------------------------ output
+// Ranks of the selected columns in index order, from a bitmap of them.
+// Thread t owns the 2^lp consecutive bitmap words [t 2^lp, (t + 1) 2^lp),
+// kept as one row of an LDS table with an odd pitch (2^lp + 1 words when
+// 2^lp > 1), so the lanes of a wave reading word j of their own rows hit
+// distinct banks.  A block scan of the rows' popcounts gives each row's
+// first rank.  A column's rank adds the popcounts before its word in the
+// row (with 4 or more words per row, from a table of them, 16-bit, written
+// by the row's owner) and the bits below it in its word.
+template <int WG>
+struct ColRanks {
+    static_assert(WG <= 512, "one first rank per thread in Smem::tbase");
+    u32* bm;        // the bitmap table: WG rows of `pitch` words
+    uint16_t* pre;  // popcount of the row's words before each word (lp >= 2)
+    u32 lp;         // log2 of the words per row
+    u32 pitch;      // row pitch in words
+    // The words of LDS needed for n columns.
+    __device__ static u32 plan(u32 n, u32& lp, u32& pitch) {
+        const u32 words = (n + 31) / 32;
+        lp = 0;
+        while (((u32)WG << lp) < words) ++lp;
+        pitch = lp ? (1u << lp) + 1u : 1u;
+        const u32 tw = (u32)WG * pitch;
+        return lp >= 2 ? tw + tw / 2 : tw;
+    }
+    __device__ ColRanks(u32* mem, u32 lp_, u32 pitch_)
+        : bm(mem), pre(lp_ >= 2 ? (uint16_t*)(mem + (u32)WG * pitch_) : nullptr), lp(lp_), pitch(pitch_) {}
+    __device__ u32 table_words() const { return (u32)WG * pitch; }
+    __device__ void mark(u32 c) const {
+        const u32 w = c >> 5;
+        atomicOr(&bm[(w >> lp) * pitch + (w & ((1u << lp) - 1u))], 1u << (c & 31));
+    }
+    // Popcount of this thread's row (and, with 4 or more words, its prefix table).
+    __device__ u32 row_count() const {
+        const u32 r0 = threadIdx.x * pitch;
+        if (lp == 0) return __popc(bm[r0]);
+        if (lp == 1) return __popc(bm[r0]) + __popc(bm[r0 + 1]);
+        const u32 per = 1u << lp;
+        u32 s = 0;
+        for (u32 j0 = 0; j0 < per; j0 += 4) {
+            u32 x[4];
+#pragma unroll
+            for (u32 u = 0; u < 4; ++u) x[u] = bm[r0 + j0 + u];
+#pragma unroll
+            for (u32 u = 0; u < 4; ++u) {
+                pre[r0 + j0 + u] = (uint16_t)s;
+                s += __popc(x[u]);
+            }
+        }
+        return s;
+    }
+    // Rank of selected column c, given each row's first rank in `base`.
+    // Call after a barrier that follows row_count.
+    __device__ u32 rank(u32 c, const u32* base) const {
+        const u32 w = c >> 5, t = w >> lp, wj = w & ((1u << lp) - 1u), sl = t * pitch + wj;
+        const u32 below = __popc(bm[sl] & ((1u << (c & 31)) - 1u));
+        if (lp == 0) return base[t] + below;
+        if (lp == 1) return base[t] + below + (wj ? __popc(bm[sl - 1]) : 0u);
+        return base[t] + (u32)pre[sl] + below;
+    }
+};
+
 // Writes the k entries of buf[0, k).  Index order, when asked for, comes
 // from a bitmap of the selected columns and a prefix popcount over it (when
 // the row's bitmap fits in the free LDS), else from a bitonic sort.
@@ -699,34 +760,21 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
         }
         return;
     }
-    const u32 words = (n + 31) / 32;
-    if (!(flags & kFlagBitonic) && (u64)k * 8 + (u64)words * 8 <= (u64)CAP * 8) {
-        u32* bm = (u32*)(sm.buf + k);
-        u32* pre = bm + words;
-        for (u32 w = tid; w < words; w += WG) bm[w] = 0;
+    u32 lp, pitch;
+    const u32 need = ColRanks<WG>::plan(n, lp, pitch);
+    if (!(flags & kFlagBitonic) && (u64)k * 2 + need <= (u64)CAP * 2) {
+        const ColRanks<WG> cr((u32*)(sm.buf + k), lp, pitch);
+        for (u32 w = tid; w < cr.table_words(); w += WG) cr.bm[w] = 0;
         __syncthreads();
-        for (u32 i = tid; i < k; i += WG) {
-            const u32 c = comp_col<E>(sm.buf[i]);
-            atomicOr(&bm[c >> 5], 1u << (c & 31));
-        }
+        for (u32 i = tid; i < k; i += WG) cr.mark(comp_col<E>(sm.buf[i]));
         __syncthreads();
-        const u32 per = (words + WG - 1) / WG;
-        const u32 w0 = tid * per;
-        u32 s = 0;
-        for (u32 j = 0; j < per; ++j)
-            if (w0 + j < words) s += __popc(bm[w0 + j]);
         u32 tot;
-        u32 run = block_excl_scan<WG, CAP>(sm, s, &tot);
-        for (u32 j = 0; j < per; ++j)
-            if (w0 + j < words) {
-                pre[w0 + j] = run;
-                run += __popc(bm[w0 + j]);
-            }
+        sm.tbase[tid] = block_excl_scan<WG, CAP>(sm, cr.row_count(), &tot);
         __syncthreads();
         for (u32 i = tid; i < k; i += WG) {
             const u64 e = sm.buf[i];
             const u32 c = comp_col<E>(e);
-            const u32 pos = pre[c >> 5] + __popc(bm[c >> 5] & ((1u << (c & 31)) - 1u));
+            const u32 pos = cr.rank(c, sm.tbase);
             out_idx[pos] = (int32_t)c;
             if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
         }
@@ -979,45 +1027,37 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
         }
         return;
     }
-    const u32 words = (n + 31) / 32;
+    u32 lp, pitch;
+    const u32 need = ColRanks<WG>::plan(n, lp, pitch);
     u32* bm = nullptr;
     DSTK_PHASE(22);
     if (!(flags & kFlagBitonic)) {
-        if (words <= (u32)kBins) bm = sm.hist;
-        else if ((u64)cnt * 2 + words <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
+        if (need <= (u32)kHistWords) bm = sm.hist;
+        else if ((u64)cnt * 2 + need <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
     }
     if (!bm) {
         emit_compacted<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, out_idx, out_val);
         return;
     }
+    const ColRanks<WG> cr(bm, lp, pitch);
     __syncthreads();  // the histogram may still be read by the last locate
-    for (u32 w = tid; w < words; w += WG) bm[w] = 0;
+    for (u32 w = tid; w < cr.table_words(); w += WG) bm[w] = 0;
     __syncthreads();
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
-        if (e >= T) {
-            const u32 c = comp_col<E>(e);
-            atomicOr(&bm[c >> 5], 1u << (c & 31));
-        }
+        if (e >= T) cr.mark(comp_col<E>(e));
     }
     __syncthreads();
     DSTK_PHASE(23);
-    const u32 per = (words + WG - 1) / WG;
-    const u32 w0 = tid * per;
-    u32 sum = 0;
-    for (u32 j = 0; j < per; ++j)
-        if (w0 + j < words) sum += __popc(bm[w0 + j]);
     u32 tot;
-    sm.tbase[tid] = block_excl_scan<WG, CAP>(sm, sum, &tot);
+    sm.tbase[tid] = block_excl_scan<WG, CAP>(sm, cr.row_count(), &tot);
     __syncthreads();
     DSTK_PHASE(24);
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
         if (e >= T) {
-            const u32 c = comp_col<E>(e), w = c >> 5, t = w / per;
-            u32 pos = sm.tbase[t];
-            for (u32 x = t * per; x < w; ++x) pos += __popc(bm[x]);
-            pos += __popc(bm[w] & ((1u << (c & 31)) - 1u));
+            const u32 c = comp_col<E>(e);
+            const u32 pos = cr.rank(c, sm.tbase);
             if (pos < k) {
                 out_idx[pos] = (int32_t)c;
                 if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
@@ -1154,6 +1194,7 @@ __device__ __noinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
     const u32 fill = __builtin_amdgcn_readfirstlane(sm.wfill[wave]);
     const u32 rb = cbase + wave * R;
     bool nan = false;
+    DSTK_PHASE(36);
     constexpr u32 kU = 4;  // entries in flight per lane
     for (u32 i0 = 0; i0 < fill; i0 += kU * kWave) {
         u64 e[kU];
@@ -1173,6 +1214,7 @@ __device__ __noinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
         }
     }
     if (nan) sm.nan = 1;  // benign race: every writer stores 1
+    DSTK_PHASE(37);
     __syncthreads();
 }
 

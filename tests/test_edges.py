@@ -205,3 +205,24 @@ def test_repeated_calls_overflow_path(pkg, oracle_mod):
         got = np.sort(idx.cpu().numpy(), axis=1)
         bad = np.nonzero(np.any(got != want, axis=1))[0]
         assert bad.size == 0, "call %d: rows %s differ" % (rep, bad[:8].tolist())
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n", [16384, 16385, 65536, 65537, 262144, 262145])
+def test_index_order_paths(pkg, oracle_mod, dtype, n):
+    # Index order from the column bitmap at each row width of its table
+    # (one word per thread up to 16384 columns, then 2, 4, ... words), and
+    # from the bitonic sort: forced, and where the table does not fit.
+    raw = make_edge_rows(dtype, 2, n, seed=n + 3, levels=64 if dtype == "bf16" else 0)
+    for k in (1, 300, 4096):
+        st, oidx, oval = oracle_mod.topk(raw, dtype, n, k, True, True, nthreads=0)
+        assert st == 0
+        for segs in (1, 3):
+            for flags in (0, 1):
+                log("index order %s n=%d k=%d segs=%d flags=%d" % (dtype, n, k, segs, flags))
+                pkg.ds_topk_set_overrides(segs, 0, flags)
+                try:
+                    gidx, gval = gpu_topk(raw, dtype, n, k, True, True)
+                finally:
+                    pkg.ds_topk_set_overrides(0, 0, 0)
+                assert_parity(raw, dtype, n, k, True, gidx, gval, oidx, oval, invariant_rows=range(raw.shape[0]))
