@@ -1827,65 +1827,106 @@ void topk_rows(Params p) {
     auto dirv = [&](u32 s_, u32 j) -> u32 {  // entries of segment s_ with digit >= d_hi - j
         return j < kDirCache ? dc[s_ * kDirCache + j] : ld_agent(&rdir[(u64)s_ * kBins + j]);
     };
-    u64 Lrow;
-    {
-        u64 lmax = 0, qmin = ~0ull;
-        for (u32 s_ = tid; s_ < S; s_ += WG) {
-            lmax = mc[s_ * 4 + 2] > lmax ? mc[s_ * 4 + 2] : lmax;
-            qmin = mc[s_ * 4 + 3] < qmin ? mc[s_ * 4 + 3] : qmin;
-        }
-        lmax = wave_max64(lmax);
-        qmin = wave_min64(qmin);
-        if (lane_id() == 0) {
-            sm.red[wave][0] = lmax;
-            sm.red[wave][1] = qmin;
-        }
-        __syncthreads();
-        lmax = 0;
-        qmin = ~0ull;
-#pragma unroll
-        for (u32 w = 0; w < WG / kWave; ++w) {
-            lmax = sm.red[w][0] > lmax ? sm.red[w][0] : lmax;
-            qmin = sm.red[w][1] < qmin ? sm.red[w][1] : qmin;
-        }
-        Lrow = lmax > qmin ? lmax : qmin;
-    }
-    DSTK_PHASE(16);
-    const u32 dL = top_digit(Lrow);
-    // row histogram of the published entries with digit >= dL, from the directories
-    for (u32 s_ = wave; s_ < S; s_ += WG / kWave) {
+    // Row histogram of the published entries, from the directories: one
+    // thread per (segment, cached directory entry), then the entries of
+    // segments with more bins than the cache holds.
+    for (u32 i = tid; i < S * kDirCache; i += WG) {
+        const u32 s_ = i / kDirCache, j = i % kDirCache;
         const u64 m0 = mc[s_ * 4];
         const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
-        if (lv == 0 || dh < dL) continue;
-        const u32 np = dh - (dl > dL ? dl : dL) + 1;
-        for (u32 j = lane_id(); j < np; j += kWave) {
-            const u32 c = dirv(s_, j) - (j ? dirv(s_, j - 1) : 0u);
+        if (lv > 0 && j <= dh - dl) {
+            const u32 c = dc[i] - (j ? dc[i - 1] : 0u);
             if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
+        }
+    }
+    {
+        // Below the row bound (the largest segment bound, or the smallest
+        // q-bound if that is larger: either leaves k entries of the row at or
+        // above it) no bin is needed; it is worked out by a wave that meets
+        // such a segment.
+        u32 dL = 0;
+        bool have_dL = false;
+        for (u32 s_ = wave; s_ < S; s_ += WG / kWave) {
+            const u64 m0 = mc[s_ * 4];
+            const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+            if (lv == 0 || dh - dl < kDirCache) continue;
+            if (!have_dL) {
+                u64 lmax = 0, qmin = ~0ull;
+                for (u32 t = lane_id(); t < S; t += kWave) {
+                    lmax = mc[t * 4 + 2] > lmax ? mc[t * 4 + 2] : lmax;
+                    qmin = mc[t * 4 + 3] < qmin ? mc[t * 4 + 3] : qmin;
+                }
+                lmax = wave_max64(lmax);
+                qmin = wave_min64(qmin);
+                dL = top_digit(lmax > qmin ? lmax : qmin);
+                have_dL = true;
+            }
+            const u32 lo = dl > dL ? dl : dL;
+            for (u32 j = kDirCache + lane_id(); dh >= lo && j <= dh - lo; j += kWave) {
+                const u32 c = dirv(s_, j) - dirv(s_, j - 1);
+                if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
+            }
         }
     }
     __syncthreads();
     DSTK_PHASE(17);
-    block_locate<WG, CAP>(sm, k, 0u, true);
-    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0];
-    DSTK_PHASE(18);
-    // entries each segment contributes: those with digit >= b1, a prefix of its list
-    u32 m = 0;
-    if (tid < S) {
-        const u64 m0 = mc[tid * 4];
-        const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[tid * 4 + 1];
-        if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(tid, dh - b1);
+    if (wave == 0) {
+        // One wave walks the bins down from the highest published one to
+        // the bin of the row's k-th entry (the counts at and above it are
+        // complete: every segment publishes all of its entries at or above
+        // its own k-th's bin, which lies at or below the row's), then gives
+        // each segment's share (its entries at or above that bin, a prefix
+        // of its list) and their offsets.
+        const u32 l = lane_id();
+        u32 dhm = 0;
+        for (u32 s_ = l; s_ < S; s_ += kWave)
+            if ((u32)mc[s_ * 4] > 0) dhm = max(dhm, (u32)mc[s_ * 4 + 1]);
+        dhm = wave_max(dhm);
+        u32 b1 = 0, r1 = 0, c1 = 0, above = 0;
+        for (u32 j0 = 0; j0 <= dhm; j0 += kWave) {
+            const u32 c = j0 + l <= dhm ? sm.hist[hidx(dhm - j0 - l)] : 0u;
+            const u32 incl = wave_incl_scan(c);
+            const u64 hit = __ballot(above + incl >= k);
+            if (hit) {
+                const u32 hl = (u32)__builtin_ctzll(hit);
+                b1 = dhm - j0 - hl;
+                c1 = __builtin_amdgcn_readlane(c, hl);
+                r1 = k - (above + __builtin_amdgcn_readlane(incl, hl) - c1);
+                break;
+            }
+            above += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        u32 carry = 0;
+        for (u32 s0 = 0; s0 < S; s0 += kWave) {
+            const u32 s_ = s0 + l;
+            u32 m = 0;
+            if (s_ < S) {
+                const u64 m0 = mc[s_ * 4];
+                const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+                if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(s_, dh - b1);
+            }
+            const u32 incl = wave_incl_scan(m);
+            if (s_ < S) sm.seg_count[s_] = carry + incl - m;
+            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        if (l == 0) {
+            sm.loc_digit[0] = b1;
+            sm.loc_r[0] = r1;
+            sm.loc_c[0] = c1;
+            sm.newtotal = carry;
+        }
     }
-    u32 total;
-    const u32 off = block_excl_scan<WG, CAP>(sm, m, &total);
-    if (tid < S) sm.seg_count[tid] = off;
     __syncthreads();
+    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0], total = sm.newtotal;
     DSTK_PHASE(13);
     if (total > (u32)CAP) {
-        merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, Lrow, k, n, p.sorted, p.retval,
+        merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
+                                   p.sorted, p.retval,
                                    p.flags, row_idx, row_val, p.flag, p.flag_value);
         return;
     }
     {
+        for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;  // zero for the selection
         constexpr int kLB = 4;  // loads in flight per thread
         for (u32 base = 0; base < total; base += WG * kLB) {
             u64 v[kLB];
