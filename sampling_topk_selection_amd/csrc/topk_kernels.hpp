@@ -1821,7 +1821,10 @@ void topk_rows(Params p) {
     for (u32 i = tid; i < S * kDirCache; i += WG)
         dc[i] = ld_agent(&rdir[(u64)(i / kDirCache) * kBins + (i % kDirCache)]);
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
-    if (tid == 0) p.ws_ticket[row] = 0;  // ready for the next call
+    if (tid == 0) {
+        p.ws_ticket[row] = 0;  // ready for the next call
+        sm.d_hi = 0;
+    }
     __syncthreads();
     DSTK_PHASE(15);
     auto dirv = [&](u32 s_, u32 j) -> u32 {  // entries of segment s_ with digit >= d_hi - j
@@ -1837,6 +1840,7 @@ void topk_rows(Params p) {
         if (lv > 0 && j <= dh - dl) {
             const u32 c = dc[i] - (j ? dc[i - 1] : 0u);
             if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
+            if (j == 0) atomicMax(&sm.d_hi, dh);
         }
     }
     {
@@ -1878,10 +1882,10 @@ void topk_rows(Params p) {
         // each segment's share (its entries at or above that bin, a prefix
         // of its list) and their offsets.
         const u32 l = lane_id();
-        u32 dhm = 0;
-        for (u32 s_ = l; s_ < S; s_ += kWave)
-            if ((u32)mc[s_ * 4] > 0) dhm = max(dhm, (u32)mc[s_ * 4 + 1]);
-        dhm = wave_max(dhm);
+        const u32 dhm = __builtin_amdgcn_readfirstlane(sm.d_hi);  // highest published bin
+        // (the first 64 segments' metadata, read ahead of the walk)
+        const u64 m0a = l < S ? mc[l * 4] : 0ull;
+        const u32 dha = l < S ? (u32)mc[l * 4 + 1] : 0u;
         u32 b1 = 0, r1 = 0, c1 = 0, above = 0;
         for (u32 j0 = 0; j0 <= dhm; j0 += kWave) {
             const u32 c = j0 + l <= dhm ? sm.hist[hidx(dhm - j0 - l)] : 0u;
@@ -1901,8 +1905,8 @@ void topk_rows(Params p) {
             const u32 s_ = s0 + l;
             u32 m = 0;
             if (s_ < S) {
-                const u64 m0 = mc[s_ * 4];
-                const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+                const u64 m0 = s0 ? mc[s_ * 4] : m0a;
+                const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = s0 ? (u32)mc[s_ * 4 + 1] : dha;
                 if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(s_, dh - b1);
             }
             const u32 incl = wave_incl_scan(m);
