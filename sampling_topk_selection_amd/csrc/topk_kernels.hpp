@@ -176,6 +176,7 @@ struct Smem {
     u64 red[16][3];    // per-wave OR / AND / MIN
     u64 L;             // admission bound: admit iff composite >= L
     u64 kth;           // k-th composite after the last compaction
+    u32 side_count;    // refine: entries gathered for it (in trash[])
     u32 count;         // entries in buf
     u32 sel_digit, sel_r, sel_c, sel_above, sel_total;
     u32 d_hi;
@@ -907,26 +908,114 @@ __device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool
     __syncthreads();
 }
 
+// The rr-th largest of the (at most 64) entries of buf[0, cnt) whose bits
+// under `mask` equal `prefix`.  Each wave counts its matches, reserves that
+// many slots of sm.trash with one atomic and writes them there; then wave w
+// compares every gathered entry with entries 8w .. 8w + 7 and adds the
+// number of larger ones to the entry's rank.  side_count must be zero on
+// entry; sm.seg_count[0, 64) is used for the ranks.
+template <int WG, int CAP>
+__device__ __noinline__ u64 side_select(Smem<CAP>& sm, u32 cnt, u64 mask, u64 prefix, u32 rr) {
+    static_assert(WG / kWave * 8 >= kWave, "eight entries compared per wave");
+    const u32 tid = threadIdx.x, l = lane_id(), wave = tid / kWave;
+    u32* const rank = sm.seg_count;
+    // one pass, four loads in flight: a bit per matching entry of this thread
+    // (entry tid + it WG for bit it; cnt <= CAP, so it < CAP / WG <= 32)
+    static_assert(CAP / WG <= 32, "one flag bit per entry of a thread");
+    u32 bits = 0, mine = 0;
+    for (u32 b0 = 0; b0 < cnt; b0 += 4 * WG) {
+        u64 e[4];
+#pragma unroll
+        for (u32 u = 0; u < 4; ++u) {
+            const u32 i = b0 + u * WG + tid;
+            e[u] = i < cnt ? sm.buf[i] : 0ull;
+        }
+#pragma unroll
+        for (u32 u = 0; u < 4; ++u) {
+            const u32 i = b0 + u * WG + tid;
+            const bool in = i < cnt && (e[u] & mask) == prefix;
+            bits |= (in ? 1u : 0u) << (b0 / WG + u);
+            mine += (u32)__popcll(__ballot(in));
+        }
+    }
+    if (tid < kWave) rank[tid] = 0;
+    if (mine) {
+        u32 base = 0;
+        if (l == 0) base = atomicAdd(&sm.side_count, mine);
+        base = __builtin_amdgcn_readfirstlane(base);
+        for (u32 it = 0; it * WG < cnt; ++it) {
+            const bool in = (bits >> it) & 1u;
+            const u64 m = __ballot(in);
+            if (!m) continue;
+            const u32 slot = base + mbcnt(m);
+            if (in && slot < (u32)kWave) sm.trash[slot] = sm.buf[it * WG + tid];  // (at most 64 match)
+            base += (u32)__popcll(m);
+        }
+    }
+    __syncthreads();
+    const u32 c = min(__builtin_amdgcn_readfirstlane(sm.side_count), (u32)kWave);
+    const u64 x = l < c ? sm.trash[l] : 0ull;
+    u32 above = 0;  // gathered entries larger than this lane's, among this wave's eight
+#pragma unroll
+    for (u32 q = 0; q < 8; ++q) {
+        const u32 j = wave * 8 + q;
+        above += (j < c && sm.trash[j] > x) ? 1u : 0u;
+    }
+    if (l < c && above) atomicAdd(&rank[l], above);
+    __syncthreads();
+    const u64 hit = __ballot(l < c && rank[l] == rr - 1);  // one lane: the entries are distinct
+    const u32 hl = hit ? (u32)__builtin_ctzll(hit) : 0u;
+    return ((u64)(u32)__builtin_amdgcn_readlane((u32)(x >> 32), hl) << 32) |
+           (u32)__builtin_amdgcn_readlane((u32)x, hl);
+}
+
+// A sub-bin this small is settled by side_select rather than another radix
+// level (measured: with more entries, the gather and the ranking cost more
+// than a level).
+constexpr u32 kSideMax = 16;
+
 // The threshold T with exactly k entries of buf[0, cnt) at or above it,
 // given the top-digit bin b1 that holds the k-th largest entry, the rank r1
-// inside it and its size c1.  Radix refinement inside the bin: 11-bit
-// digits, each window starting at the highest bit where the remaining
-// entries can still differ (taken from the OR and AND of the bin's
-// entries), so runs of bits shared by all of them (equal values, the high
-// bits of small column numbers) cost no level.  The histogram must be zero
-// on entry and is zero again on return.
-template <int WG, int CAP>
+// inside it and its size c1.  Radix refinement inside the bin with 11-bit
+// digits, each window starting at the highest bit where the bin's entries
+// still differ (taken from their OR and AND), so runs of bits shared by all
+// of them (equal values, the high bits of small column numbers) cost no
+// level.  With kFixedFirst (32-bit keys, whose 11 bits below the top digit
+// seldom tie) the first level takes those bits right away and gathers the
+// OR and AND on the way, for the levels that may follow; there, a sub-bin
+// of at most kSideMax entries that still holds the k-th is settled
+// directly by side_select (with 16-bit keys the sub-bins that remain are
+// runs of equal values, seldom that small).  The histogram must be zero on
+// entry and is zero again on return.
+template <int WG, int CAP, bool kFixedFirst = false>
 __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1) {
     if (r1 >= c1) return digit_floor(b1);  // the whole bin is kept
     const u32 tid = threadIdx.x, wave = tid / kWave;
     constexpr int kTop = 64 - kHistBits;
+    constexpr int kSh1 = kTop - kHistBits;
+    if (kFixedFirst && tid == 0) sm.side_count = 0;  // (read after the barriers below)
+    u64 P = digit_floor(b1);  // bits of T fixed so far: those at or above `fixed`
+    int fixed = kTop;
+    u32 r = r1;
     u64 o = 0, a = ~0ull;
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
         if (top_digit(e) == b1) {
             o |= e;
             a &= e;
+            if constexpr (kFixedFirst) atomicAdd(&sm.hist[hidx((u32)(e >> kSh1) & (kBins - 1))], 1u);
         }
+    }
+    if constexpr (kFixedFirst) {
+        __syncthreads();
+        DSTK_PHASE(20);
+        block_locate<WG, CAP>(sm, r1, 0u, true);
+        P |= (u64)sm.loc_digit[0] << kSh1;
+        fixed = kSh1;
+        r = sm.loc_r[0];
+        DSTK_PHASE(21);
+        if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
+        if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(kSh1), P, r);
     }
     {
         const u32 ohi = wave_or((u32)(o >> 32)), olo = wave_or((u32)o);
@@ -943,11 +1032,8 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         O |= sm.red[w][0];
         A &= sm.red[w][1];
     }
-    u64 D = (O ^ A) & low_mask(kTop);  // bits where entries of the bin differ
-    DSTK_PHASE(20);
-    u64 P = digit_floor(b1);           // bits fixed so far (above `fixed`)
-    int fixed = kTop;
-    u32 r = r1;
+    u64 D = (O ^ A) & low_mask(fixed);  // bits below those fixed where entries of the bin differ
+    if constexpr (!kFixedFirst) DSTK_PHASE(20);
     for (int level = 0; level < 64 / kHistBits + 2; ++level) {
         // D != 0 here: the remaining set has at least two (distinct) entries
         const int hb = 63 - __clzll((long long)D);
@@ -962,9 +1048,11 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         block_locate<WG, CAP>(sm, r, 0u, true);
         const u32 d = sm.loc_digit[0], rr = sm.loc_r[0], c = sm.loc_c[0];
         P |= (u64)d << sh;
-        DSTK_PHASE(21);
+        if constexpr (!kFixedFirst) DSTK_PHASE(21);
         fixed = sh;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
+        if constexpr (kFixedFirst)
+            if (c <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh), P, rr);
         r = rr;
         D &= low_mask(sh);
     }
@@ -1454,7 +1542,7 @@ template <class E, int WG, int CAP>
 __device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 n, int sorted,
                                              int retval, int flags, int32_t* row_idx, void* row_val, int32_t* flag,
                                              int32_t flag_value) {
-    const u64 T = refine<WG, CAP>(sm, cnt, b1, r1, c1);
+    const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
     DSTK_PHASE(5);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     __syncthreads();
@@ -1892,7 +1980,7 @@ void topk_rows(Params p) {
             const u32 incl = wave_incl_scan(c);
             const u64 hit = __ballot(above + incl >= k);
             if (hit) {
-                const u32 hl = (u32)__builtin_ctzll(hit);
+                const u32 hl = hit ? (u32)__builtin_ctzll(hit) : 0u;
                 b1 = dhm - j0 - hl;
                 c1 = __builtin_amdgcn_readlane(c, hl);
                 r1 = k - (above + __builtin_amdgcn_readlane(incl, hl) - c1);
