@@ -977,10 +977,11 @@ constexpr u32 kSideMax = 16;
 // The threshold T with exactly k entries of buf[0, cnt) at or above it,
 // given the top-digit bin b1 that holds the k-th largest entry, the rank r1
 // inside it and its size c1.  Radix refinement inside the bin with 11-bit
-// digits, each window starting at the highest bit where the bin's entries
-// still differ (taken from their OR and AND), so runs of bits shared by all
-// of them (equal values, the high bits of small column numbers) cost no
-// level.  With kFixedFirst (32-bit keys, whose 11 bits below the top digit
+// digits made only of bits where the bin's entries still differ (taken
+// from their OR and AND): the highest run of such bits and, when it is
+// shorter than 11, the next such bits below it, so runs of bits shared by
+// all of them (equal values, the high bits of small column numbers) cost
+// no level.  With kFixedFirst (32-bit keys, whose 11 bits below the top digit
 // seldom tie) the first level takes those bits right away and gathers the
 // OR and AND on the way, for the levels that may follow; there, a sub-bin
 // of at most kSideMax entries that still holds the k-th is settled
@@ -1037,24 +1038,51 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
     for (int level = 0; level < 64 / kHistBits + 2; ++level) {
         // D != 0 here: the remaining set has at least two (distinct) entries
         const int hb = 63 - __clzll((long long)D);
-        const int sh = hb >= kHistBits - 1 ? hb - (kHistBits - 1) : 0;
         P |= A & (low_mask(fixed) & ~low_mask(hb + 1));  // bits shared by the whole set
         const u64 pm = ~low_mask(hb + 1);
-        for (u32 i = tid; i < cnt; i += WG) {
-            const u64 e = sm.buf[i];
-            if ((e & pm) == P) atomicAdd(&sm.hist[hidx((u32)(e >> sh) & (kBins - 1))], 1u);
+        // The digit: D's run of set bits from hb down (at most 11 bits,
+        // [lo1, hb]) and, when that is shorter, the highest bits of D below
+        // it ([sh2, hb2]); the bits between are shared by the whole set, so
+        // the digit orders the set like the composites do.
+        const u64 z = ~D & low_mask(hb + 1);
+        int lo1 = z ? 64 - __clzll((long long)z) : 0;
+        lo1 = lo1 > hb - (kHistBits - 1) ? lo1 : hb - (kHistBits - 1);
+        const int len1 = hb - lo1 + 1;
+        const u64 D2 = D & low_mask(lo1);
+        int len2 = 0, hb2 = lo1 - 1;
+        if (len1 < kHistBits && D2) {
+            hb2 = 63 - __clzll((long long)D2);
+            len2 = kHistBits - len1 < hb2 + 1 ? kHistBits - len1 : hb2 + 1;
+        }
+        if (len2 == 0) {  // one part: 11 bits from hb down
+            lo1 = hb >= kHistBits - 1 ? hb - (kHistBits - 1) : 0;
+            hb2 = lo1 - 1;
+        }
+        const int sh2 = hb2 - len2 + 1;  // (= lo1 with one part)
+        if (len2 == 0) {
+            for (u32 i = tid; i < cnt; i += WG) {
+                const u64 e = sm.buf[i];
+                if ((e & pm) == P) atomicAdd(&sm.hist[hidx((u32)(e >> lo1) & (kBins - 1))], 1u);
+            }
+        } else {
+            const u64 m1 = low_mask(len1), m2 = low_mask(len2);
+            for (u32 i = tid; i < cnt; i += WG) {
+                const u64 e = sm.buf[i];
+                if ((e & pm) == P) atomicAdd(&sm.hist[hidx((u32)((((e >> lo1) & m1) << len2) | ((e >> sh2) & m2)))], 1u);
+            }
         }
         __syncthreads();
         block_locate<WG, CAP>(sm, r, 0u, true);
         const u32 d = sm.loc_digit[0], rr = sm.loc_r[0], c = sm.loc_c[0];
-        P |= (u64)d << sh;
+        P |= ((u64)(d >> len2) << lo1) | ((u64)(d & (u32)low_mask(len2)) << sh2);
+        P |= A & (low_mask(lo1) & ~low_mask(hb2 + 1));  // the shared bits between the two parts
         if constexpr (!kFixedFirst) DSTK_PHASE(21);
-        fixed = sh;
+        fixed = sh2;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
         if constexpr (kFixedFirst)
-            if (c <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh), P, rr);
+            if (c <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
         r = rr;
-        D &= low_mask(sh);
+        D &= low_mask(sh2);
     }
     return P;
 }
