@@ -56,12 +56,14 @@ def max_threads() -> int:
     return _load().oracle_max_threads()
 
 
-def topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: bool = True,
+def topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index=True,
          return_value: bool = True, nthreads: int = 1
          ) -> Tuple[int, np.ndarray, Optional[np.ndarray]]:
     """Top-k of each row of ``raw`` ([batch, row_stride] raw element bits:
-    uint16 for bf16, float32 for fp32).  Returns (status, indices int32
-    [batch, k], values [batch, k] of raw's dtype or None)."""
+    uint16 for bf16, float32 for fp32).  ``sorted_index``: 0/False any
+    order, 1/True ascending index, 2 by value (largest first).  Returns
+    (status, indices int32 [batch, k], values [batch, k] of raw's dtype or
+    None)."""
     lib = _load()
     raw = np.ascontiguousarray(raw)
     want = np.uint16 if dtype == "bf16" else np.float32
@@ -71,6 +73,6 @@ def topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: bool = True,
     idx = np.zeros((batch, k), dtype=np.int32)
     val = np.zeros((batch, k), dtype=want) if return_value else None
     st = lib.oracle_topk(raw.ctypes.data, _DT[dtype], batch, n, row_stride, k,
-                         int(bool(sorted_index)), int(bool(return_value)), idx.ctypes.data,
+                         int(sorted_index), int(bool(return_value)), idx.ctypes.data,
                          val.ctypes.data if val is not None else None, int(nthreads))
     return st, idx, val

@@ -18,10 +18,12 @@
  *       v_i and v_j are the same value and i < j (lower index wins a tie).
  *     +inf ranks first and -inf last, like any other value.
  *   - The selected set of a row is the k elements of rank < k.
- *   - sorted_index: the selected indices are written in ascending order
- *     (the aiutil project card, 关键技术亮点 item 2, names sorting by index).
- *     Otherwise they are written in descending rank order (any order is
- *     correct; this one is just convenient).
+ *   - Output order (the `sorted_index` argument): 1 writes the selected
+ *     indices in ascending order (the aiutil project card, 关键技术亮点 item
+ *     2, names sorting by index); 2 writes them by value, in the order above
+ *     (largest first; the same page names sorting by value as the other
+ *     option); 0 leaves the order free, and the oracle then also writes the
+ *     order above (any order is correct; this one is just convenient).
  *   - Values are exact bit copies of the input elements at the chosen indices.
  *   - NaN: any NaN of either sign in columns [0, n) of any row makes the call
  *     return ORACLE_NAN (the pages say NaN checking is always on; see the
@@ -101,7 +103,7 @@ static int one_row(const void* row, int dtype, int64_t n, int32_t k, int sorted_
         }
     }
     qsort(it, (size_t)n, sizeof(item), by_rank);
-    if (sorted_index) qsort(it, (size_t)k, sizeof(item), by_index);
+    if (sorted_index == 1) qsort(it, (size_t)k, sizeof(item), by_index);
     const size_t es = dtype == ORACLE_BF16 ? 2 : 4;
     for (int32_t j = 0; j < k; ++j) {
         out_idx[j] = (int32_t)it[j].i;
@@ -122,7 +124,7 @@ static int one_row(const void* row, int dtype, int64_t n, int32_t k, int sorted_
 int oracle_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
                 int32_t k, int sorted_index, int return_value, int32_t* out_idx,
                 void* out_val, int nthreads) {
-    if ((dtype != ORACLE_BF16 && dtype != ORACLE_F32) || batch < 0 || n < 1 || k < 1 ||
+    if ((dtype != ORACLE_BF16 && dtype != ORACLE_F32) || sorted_index < 0 || sorted_index > 2 || batch < 0 || n < 1 || k < 1 ||
         k > n || row_stride < n || !in || !out_idx || (return_value && !out_val))
         return ORACLE_BAD_ARG;
     const size_t es = dtype == ORACLE_BF16 ? 2 : 4;

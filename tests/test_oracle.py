@@ -17,6 +17,7 @@ import tempfile
 import numpy as np
 import pytest
 
+import brute
 from brute import topk_set_loop, topk_set_numpy
 from invariants import check_topk_row, check_values_row
 from workloads import CONFIGS, bf16_bits_from_f32, make_edge_rows, make_workload
@@ -193,6 +194,24 @@ def test_unsorted_is_rank_order(oracle_mod):
     assert sorted(b[0].tolist()) == a[0].tolist()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_value_order_is_rank_order(oracle_mod, dtype):
+    # Order 2 lists the selection by value: the j-th output has brute-force
+    # rank j (ties by lower index, +0 before -0), checked position by position.
+    for seed in range(6):
+        n = 40 + 13 * seed
+        raw = make_edge_rows(dtype, 1, n, seed=100 + seed, levels=5 if seed % 2 else 0, specials=0.1)
+        vals = brute.decode(raw[0, :n], dtype)
+        ranks = [sum(1 for j in range(n) if j != i and brute.precedes(vals[j], j, vals[i], i)) for i in range(n)]
+        by_rank = sorted(range(n), key=lambda i: ranks[i])
+        for k in (1, 7, n // 2, n):
+            st, idx, val = oracle_mod.topk(raw, dtype, n, k, sorted_index=2)
+            assert st == 0
+            assert idx[0].tolist() == by_rank[:k]
+            assert np.array_equal(val[0], raw[0, idx[0]])
+    assert oracle_mod.topk(make_edge_rows("f32", 1, 16, seed=0), "f32", 16, 4, sorted_index=3)[0] == oracle_mod.BAD_ARG
+
+
 # ---------------------------------------------------------------- planted mistakes
 _MUTANTS = {
     "tie_to_higher_index": ("if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
@@ -201,6 +220,7 @@ _MUTANTS = {
     "drops_last_column": ("for (int64_t c = 0; c < n; ++c) {", "for (int64_t c = 0; c < n - 1; ++c) {"),
     "bf16_low_half": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;"),
     "no_nan_check": ("if (isnan(it[c].v)) {", "if (0) {"),
+    "value_order_by_index": ("if (sorted_index == 1) qsort", "if (sorted_index) qsort"),
 }
 
 
@@ -223,6 +243,7 @@ def _pins_pass(oracle_mod):
         test_closed_form_constant(oracle_mod, "bf16")
         test_nan_status(oracle_mod, "bf16")
         test_nan_status(oracle_mod, "f32")
+        test_value_order_is_rank_order(oracle_mod, "bf16")
     except AssertionError:
         return False
     return True
