@@ -42,11 +42,21 @@ enum ds_topk_dtype {
     DS_DTYPE_F32 = 1   /* IEEE binary32 */
 };
 
+/* Output order within a row (the `sorted_index` argument). */
+enum ds_topk_order {
+    DS_ORDER_NONE = 0,  /* any order; it may differ between calls */
+    DS_ORDER_INDEX = 1, /* ascending column index */
+    DS_ORDER_VALUE = 2  /* by value, largest first, in the selection's own
+                           order (see the top of this file): equal values
+                           by lower index, +0 before -0 */
+};
+
 /* Status codes returned by every entry point. */
 enum ds_topk_status {
     DS_OK = 0,
     /* A null `in` or `out_idx`; `return_value` set with a null `out_val`;
-       batch < 0; n < 1; k < 1; k > n; row_stride < n. */
+       batch < 0; n < 1; k < 1; k > n; row_stride < n; sorted_index not a
+       ds_topk_order. */
     DS_ERR_INVALID_ARGUMENT = 1,
     /* k > 4096 (CSDN page, section 三: small top-k only, at most 4096);
        an unknown dtype; n > 2^31 - 1 (indices are int32). */
@@ -83,11 +93,14 @@ enum ds_topk_status {
  *   row_stride   elements between row starts, >= n; row_stride * element
  *                size must be a multiple of 16 bytes.
  *   k            1 <= k <= min(n, 4096).
- *   sorted_index nonzero: each row's k indices are written in ascending
- *                order (aiutil card, 关键技术亮点 item 2: sorted output costs
- *                speed, so leave it off unless needed).  Zero: the order
- *                within a row is unspecified and may differ between calls;
- *                the set is always the same.
+ *   sorted_index a ds_topk_order.  DS_ORDER_INDEX: each row's k indices
+ *                are written in ascending order (aiutil card, 关键技术亮点
+ *                item 2, which names sorting by index or by value and notes
+ *                that sorted output costs speed, so leave it off unless
+ *                needed).  DS_ORDER_VALUE: largest value first, ties by
+ *                lower index.  DS_ORDER_NONE: the order within a row is
+ *                unspecified and may differ between calls; the set is
+ *                always the same.
  *   return_value nonzero: write the selected values to out_val.  Zero: skip
  *                that output (zh-TW page, section DeepSelect:
  *                return_value=False skips the values and is faster).

@@ -34,6 +34,9 @@ DS_ERR_UNSUPPORTED = 2
 DS_ERR_MISALIGNED = 3
 DS_ERR_NAN = 4
 DS_ERR_HIP = 5
+DS_ORDER_NONE = 0
+DS_ORDER_INDEX = 1
+DS_ORDER_VALUE = 2
 
 MAX_K = 4096
 
@@ -158,19 +161,29 @@ def _marshal(x: torch.Tensor, k: int, n: Optional[int]):
     return x, _TORCH_DT[x.dtype], batch, n, row_stride
 
 
+def _order(sorted_index: bool, sorted_value: bool) -> int:
+    if sorted_index and sorted_value:
+        raise ValueError("sorted_index and sorted_value are exclusive")
+    return DS_ORDER_VALUE if sorted_value else DS_ORDER_INDEX if sorted_index else DS_ORDER_NONE
+
+
 def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: bool = True,
-         n: Optional[int] = None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+         n: Optional[int] = None, sorted_value: bool = False) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """Top-k of each row of ``x`` ([batch, n], bf16 or fp32, on the device).
 
     Returns ``(values, indices)``; values is None when ``return_value`` is
-    False.  Indices are int32.  ``n`` restricts the selection to the first n
-    columns (the rest of each row is padding).  Blocks until done.
+    False.  Indices are int32.  ``sorted_index`` writes each row's indices in
+    ascending order, ``sorted_value`` largest value first (ties by lower
+    index); neither leaves the order free.  ``n`` restricts the selection to
+    the first n columns (the rest of each row is padding).  Blocks until
+    done.
     """
+    order = _order(sorted_index, sorted_value)
     x, dt, batch, n, row_stride = _marshal(x, k, n)
     idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
     val = torch.empty((batch, k), dtype=x.dtype, device=x.device) if return_value else None
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = ds_topk(x.data_ptr(), dt, batch, n, row_stride, k, int(bool(sorted_index)), int(bool(return_value)),
+    st = ds_topk(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)),
                  idx.data_ptr(), val.data_ptr() if val is not None else None, stream)
     _check(st)
     return val, idx
@@ -178,13 +191,14 @@ def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: b
 
 def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: bool = False,
                return_value: bool = True, n: Optional[int] = None,
-               out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor]] = None
+               out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor]] = None, sorted_value: bool = False
                ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """Enqueue the selection on the current stream without waiting.
 
     ``status`` is a zero-initialised int32 device tensor (one element); the
     kernels store DS_ERR_NAN there if a row holds NaN.  ``out`` may supply
-    preallocated (values, indices)."""
+    preallocated (values, indices).  Order arguments as for topk()."""
+    order = _order(sorted_index, sorted_value)
     x, dt, batch, n, row_stride = _marshal(x, k, n)
     if out is not None:
         val, idx = out
@@ -194,7 +208,7 @@ def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: b
     if status.dtype != torch.int32 or not status.is_cuda:
         raise ValueError("status must be an int32 device tensor")
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = ds_topk_async(x.data_ptr(), dt, batch, n, row_stride, k, int(bool(sorted_index)),
+    st = ds_topk_async(x.data_ptr(), dt, batch, n, row_stride, k, order,
                        int(bool(return_value)), idx.data_ptr(), val.data_ptr() if val is not None else None,
                        status.data_ptr(), stream)
     _check(st)

@@ -228,6 +228,8 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
     g_err.clear();
     int st = validate(dtype, batch, n, row_stride, k);
     if (st) return st;
+    if (sorted_index < DS_ORDER_NONE || sorted_index > DS_ORDER_VALUE)
+        return fail(DS_ERR_INVALID_ARGUMENT, "sorted_index %d is not a ds_topk_order", sorted_index);
     if (!in) return fail(DS_ERR_INVALID_ARGUMENT, "in is NULL");
     if (!out_idx) return fail(DS_ERR_INVALID_ARGUMENT, "out_idx is NULL");
     if (return_value && !out_val) return fail(DS_ERR_INVALID_ARGUMENT, "return_value set but out_val is NULL");
@@ -268,7 +270,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.seg_vecs = pl.seg_vecs;
         prm.n_vec = pl.n_vec;
         prm.seed = g_tile_seed.load();
-        prm.sorted = sorted_index ? 1 : 0;
+        prm.sorted = sorted_index;
         prm.retval = return_value ? 1 : 0;
         prm.out_idx = out_idx + r0 * k;
         prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
@@ -327,11 +329,12 @@ const char* ds_topk_last_error(void) { return g_err.c_str(); }
 
 int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
                      int return_value, ds_topk_plan* plan) {
-    (void)sorted_index;
     (void)return_value;
     g_err.clear();
     const int st = validate(dtype, batch, n, row_stride, k);
     if (st) return st;
+    if (sorted_index < DS_ORDER_NONE || sorted_index > DS_ORDER_VALUE)
+        return fail(DS_ERR_INVALID_ARGUMENT, "sorted_index %d is not a ds_topk_order", sorted_index);
     if (!plan) return fail(DS_ERR_INVALID_ARGUMENT, "plan is NULL");
     Plan pl;
     make_plan(dtype, batch, n, k, &pl);

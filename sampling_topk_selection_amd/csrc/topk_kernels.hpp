@@ -160,6 +160,8 @@ __device__ __forceinline__ bool nan_slot(Elem<2>, const u32 (&dw)[4]) {
 constexpr int kHistBits = 11;  // radix-select digit width
 constexpr int kBins = 1 << kHistBits;
 constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
+constexpr int kOrderIndex = 1;   // Params::sorted: ascending column index
+constexpr int kOrderValue = 2;   // Params::sorted: largest composite first
 
 // Histogram storage is transposed with a padded row: bin d lives at
 // ((d mod 32) * 65 + d / 32), so atomics on consecutive bins (the hot bins
@@ -744,9 +746,11 @@ struct ColRanks {
     }
 };
 
-// Writes the k entries of buf[0, k).  Index order, when asked for, comes
-// from a bitmap of the selected columns and a prefix popcount over it (when
-// the row's bitmap fits in the free LDS), else from a bitonic sort.
+// Writes the k entries of buf[0, k) in the order `sorted` asks for
+// (0, kOrderIndex or kOrderValue).  Index order comes from a bitmap of the
+// selected columns and a prefix popcount over it (when the row's bitmap
+// fits in the free LDS), else from a bitonic sort; value order from a
+// bitonic sort of the composites.
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
                      void* out_val) {
@@ -763,7 +767,7 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
     }
     u32 lp, pitch;
     const u32 need = ColRanks<WG>::plan(n, lp, pitch);
-    if (!(flags & kFlagBitonic) && (u64)k * 2 + need <= (u64)CAP * 2) {
+    if (sorted == kOrderIndex && !(flags & kFlagBitonic) && (u64)k * 2 + need <= (u64)CAP * 2) {
         const ColRanks<WG> cr((u32*)(sm.buf + k), lp, pitch);
         for (u32 w = tid; w < cr.table_words(); w += WG) cr.bm[w] = 0;
         __syncthreads();
@@ -781,11 +785,14 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
         }
         return;
     }
+    // Bitonic sort, ascending, of (column, key) for index order, or of the
+    // complemented composites for value order (largest composite first);
+    // padding ~0 sorts last either way.
     u32 P = 1;
     while (P < k) P <<= 1;
     for (u32 i = tid; i < P; i += WG) {
         const u64 e = i < k ? sm.buf[i] : 0ull;
-        sm.buf[i] = i < k ? (((u64)comp_col<E>(e) << 32) | comp_key<E>(e)) : ~0ull;
+        sm.buf[i] = i >= k ? ~0ull : sorted == kOrderValue ? ~e : (((u64)comp_col<E>(e) << 32) | comp_key<E>(e));
     }
     __syncthreads();
     for (u32 size = 2; size <= P; size <<= 1) {
@@ -805,8 +812,13 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
     }
     for (u32 i = tid; i < k; i += WG) {
         const u64 s = sm.buf[i];
-        out_idx[i] = (int32_t)(u32)(s >> 32);
-        if (retval) ov[i] = (VT)E::bits((u32)s);
+        if (sorted == kOrderValue) {
+            out_idx[i] = (int32_t)comp_col<E>(~s);
+            if (retval) ov[i] = (VT)E::bits(comp_key<E>(~s));
+        } else {
+            out_idx[i] = (int32_t)(u32)(s >> 32);
+            if (retval) ov[i] = (VT)E::bits((u32)s);
+        }
     }
 }
 
@@ -1147,7 +1159,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
     const u32 need = ColRanks<WG>::plan(n, lp, pitch);
     u32* bm = nullptr;
     DSTK_PHASE(22);
-    if (!(flags & kFlagBitonic)) {
+    if (sorted == kOrderIndex && !(flags & kFlagBitonic)) {
         if (need <= (u32)kHistWords) bm = sm.hist;
         else if ((u64)cnt * 2 + need <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
     }
@@ -1514,7 +1526,7 @@ struct Params {
     int32_t seg_vecs;  // 16-byte vectors per segment
     int32_t n_vec;     // 16-byte vectors per row holding valid columns
     uint32_t seed;
-    int32_t sorted;
+    int32_t sorted;    // output order: 0, kOrderIndex or kOrderValue
     int32_t retval;
     int32_t* out_idx;
     void* out_val;

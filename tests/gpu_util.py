@@ -33,20 +33,23 @@ def to_host_bits(val, dtype: str) -> np.ndarray:
     return val.cpu().numpy()
 
 
-def gpu_topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: bool, return_value: bool):
+def gpu_topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index, return_value: bool):
+    """sorted_index: 0/False any order, 1/True ascending index, 2 by value."""
     import sampling_topk_selection_amd as pkg
 
     x = to_device(raw, dtype)
-    val, idx = pkg.topk(x, k, sorted_index=sorted_index, return_value=return_value, n=n)
+    order = int(sorted_index)
+    val, idx = pkg.topk(x, k, sorted_index=order == 1, sorted_value=order == 2, return_value=return_value, n=n)
     gidx = idx.cpu().numpy()
     gval = to_host_bits(val, dtype) if val is not None else None
     return gidx, gval
 
 
-def assert_parity(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: bool, gidx: np.ndarray,
+def assert_parity(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index, gidx: np.ndarray,
                   gval, oidx: np.ndarray, oval, invariant_rows=None) -> None:
-    """Indices: same set per row (same order too when sorted); values: bit
-    copies of the inputs at the returned indices, equal to the oracle's."""
+    """Indices: same set per row (same order too when an order is asked for:
+    sorted_index 1 by index, 2 by value); values: bit copies of the inputs
+    at the returned indices, equal to the oracle's."""
     batch = raw.shape[0]
     assert gidx.shape == (batch, k), gidx.shape
     if sorted_index:
@@ -68,6 +71,6 @@ def assert_parity(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index: boo
             ov = np.ascontiguousarray(oval).view(np.uint16 if dtype == "bf16" else np.uint32)
             assert np.array_equal(gv, ov)
     for r in (invariant_rows if invariant_rows is not None else []):
-        check_topk_row(raw[r], dtype, n, k, gidx[r], sorted_index=sorted_index)
+        check_topk_row(raw[r], dtype, n, k, gidx[r], sorted_index=int(sorted_index) == 1)
         if gval is not None:
             check_values_row(raw[r], gidx[r], gval[r])

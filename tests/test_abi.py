@@ -87,6 +87,11 @@ def test_pointer_errors(pkg):
     assert pkg.ds_topk(FAKE, BF, 4, 64, 64, 8, 0, 1, FAKE, None, None) == 1  # values wanted, no buffer
     assert pkg.ds_topk(FAKE + 2, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None) == 3  # misaligned base
     assert pkg.ds_topk_async(FAKE, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None, None) == 1  # no status word
+    for order in (-1, 3):  # not a ds_topk_order
+        assert pkg.ds_topk(FAKE, BF, 4, 64, 64, 8, order, 0, FAKE, None, None) == 1
+        assert pkg.ds_topk_plan_for(BF, 4, 64, 64, 8, order)[0] == 1
+    for order in (pkg.DS_ORDER_NONE, pkg.DS_ORDER_INDEX, pkg.DS_ORDER_VALUE):
+        assert pkg.ds_topk_plan_for(BF, 4, 64, 64, 8, order)[0] == 0
 
 
 def test_k_limits_from_pages(pkg):

@@ -226,3 +226,17 @@ def test_index_order_paths(pkg, oracle_mod, dtype, n):
                 finally:
                     pkg.ds_topk_set_overrides(0, 0, 0)
                 assert_parity(raw, dtype, n, k, True, gidx, gval, oidx, oval, invariant_rows=range(raw.shape[0]))
+
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("levels", [0, 3, 64])
+def test_value_order_edges(pkg, oracle_mod, dtype, levels):
+    # Value order through every path: short and long rows, ties, +-0, +-inf,
+    # one segment and several, k up to 4096.
+    for n in (1, 9, 1001, 70001):
+        raw = make_edge_rows(dtype, 3, n, seed=n + levels, levels=levels, specials=0.05)
+        for k in sorted({1, min(n, 33), min(n, 4096)}):
+            log("value order %s levels=%d n=%d k=%d" % (dtype, levels, n, k))
+            for segs in (0, 1, 4):
+                _check(pkg, oracle_mod, raw, dtype, n, k, 2, segs)

@@ -65,3 +65,22 @@ def test_sorted_and_unsorted_agree(pkg, oracle_mod, cfg):
     assert np.array_equal(a, np.sort(b, axis=1))
     order = np.argsort(b, axis=1)
     assert np.array_equal(av, np.take_along_axis(bv, order, axis=1))
+
+
+@pytest.mark.parametrize("cfg", sorted(CONFIGS))
+@pytest.mark.parametrize("segs", [0, 1, 3])
+def test_value_order(pkg, oracle_mod, cfg, segs):
+    # Largest value first, ties by lower index: one order, compared exactly.
+    batch = min(CONFIGS[cfg]["batch"], 8)
+    w = make_workload(cfg, batch=batch)
+    log("value order %s segments=%d batch=%d" % (cfg, segs, batch))
+    st, oidx, oval = oracle_mod.topk(w.raw, w.dtype, w.n, w.k, 2, True, nthreads=0)
+    assert st == 0
+    pkg.ds_topk_set_overrides(segs, 0)
+    try:
+        for rv in (True, False):
+            gidx, gval = gpu_topk(w.raw, w.dtype, w.n, w.k, 2, rv)
+            assert_parity(w.raw, w.dtype, w.n, w.k, 2, gidx, gval, oidx, oval if rv else None,
+                          invariant_rows=range(min(batch, 2)))
+    finally:
+        pkg.ds_topk_set_overrides(0, 0)
