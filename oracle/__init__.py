@@ -47,6 +47,10 @@ def _load():
         lib.oracle_topk.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_topk_lengths.restype = ctypes.c_int
+        lib.oracle_topk_lengths.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -75,4 +79,26 @@ def topk(raw: np.ndarray, dtype: str, n: int, k: int, sorted_index=True,
     st = lib.oracle_topk(raw.ctypes.data, _DT[dtype], batch, n, row_stride, k,
                          int(sorted_index), int(bool(return_value)), idx.ctypes.data,
                          val.ctypes.data if val is not None else None, int(nthreads))
+    return st, idx, val
+
+
+def topk_lengths(raw: np.ndarray, dtype: str, n: int, k: int, lengths, sorted_index=True,
+                 return_value: bool = True, nthreads: int = 1
+                 ) -> Tuple[int, np.ndarray, Optional[np.ndarray]]:
+    """As topk(), with row r's valid columns [0, lengths[r]) (clamped to
+    [0, n]); the other columns act as -inf and are never read."""
+    lib = _load()
+    raw = np.ascontiguousarray(raw)
+    want = np.uint16 if dtype == "bf16" else np.float32
+    if raw.dtype != want:
+        raise TypeError("raw must be %s for %s" % (np.dtype(want).name, dtype))
+    batch, row_stride = raw.shape
+    lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    if lens.shape != (batch,):
+        raise ValueError("one length per row")
+    idx = np.zeros((batch, k), dtype=np.int32)
+    val = np.zeros((batch, k), dtype=want) if return_value else None
+    st = lib.oracle_topk_lengths(raw.ctypes.data, _DT[dtype], batch, n, row_stride, k, lens.ctypes.data,
+                                 int(sorted_index), int(bool(return_value)), idx.ctypes.data,
+                                 val.ctypes.data if val is not None else None, int(nthreads))
     return st, idx, val

@@ -30,6 +30,12 @@
  *     zh-TW page "深入 DeepSeek V4.1 全新開放推論工具包", section DeepSelect).
  *     Padding columns [n, row_stride) are never looked at.
  *
+ *   - Per-row valid lengths (oracle_topk_lengths): row r holds len_r valid
+ *     columns; columns [len_r, n) act as -inf, are never read and never
+ *     NaN-checked, and their values are written as -inf (the lengths stand
+ *     in for -inf tails: the C4 decode workload's rows are valid prefixes
+ *     followed by -inf).  A length outside [0, n] is clamped to it.
+ *
  * Values are widened exactly to double (bf16 -> binary32 by a 16-bit shift,
  * then binary32 -> binary64), so every comparison is exact.
  *
@@ -89,13 +95,14 @@ static int by_index(const void* pa, const void* pb) {
     return (a->i > b->i) - (a->i < b->i);
 }
 
-/* One row: returns ORACLE_OK, ORACLE_NAN or ORACLE_NOMEM. */
-static int one_row(const void* row, int dtype, int64_t n, int32_t k, int sorted_index,
+/* One row with `len` valid columns (the rest act as -inf): returns
+   ORACLE_OK, ORACLE_NAN or ORACLE_NOMEM. */
+static int one_row(const void* row, int dtype, int64_t n, int64_t len, int32_t k, int sorted_index,
                    int return_value, int32_t* out_idx, void* out_val) {
     item* it = (item*)malloc((size_t)n * sizeof(item));
     if (!it) return ORACLE_NOMEM;
     for (int64_t c = 0; c < n; ++c) {
-        it[c].v = widen(row, dtype, c);
+        it[c].v = c < len ? widen(row, dtype, c) : -INFINITY;
         it[c].i = c;
         if (isnan(it[c].v)) {
             free(it);
@@ -105,10 +112,15 @@ static int one_row(const void* row, int dtype, int64_t n, int32_t k, int sorted_
     qsort(it, (size_t)n, sizeof(item), by_rank);
     if (sorted_index == 1) qsort(it, (size_t)k, sizeof(item), by_index);
     const size_t es = dtype == ORACLE_BF16 ? 2 : 4;
+    const uint16_t ninf16 = 0xFF80;
+    const uint32_t ninf32 = 0xFF800000u;
     for (int32_t j = 0; j < k; ++j) {
         out_idx[j] = (int32_t)it[j].i;
-        if (return_value)
-            memcpy((char*)out_val + es * j, (const char*)row + es * it[j].i, es);
+        if (return_value) {
+            const void* src = it[j].i < len ? (const void*)((const char*)row + es * it[j].i)
+                              : dtype == ORACLE_BF16 ? (const void*)&ninf16 : (const void*)&ninf32;
+            memcpy((char*)out_val + es * j, src, es);
+        }
     }
     free(it);
     return ORACLE_OK;
@@ -121,9 +133,24 @@ static int one_row(const void* row, int dtype, int64_t n, int32_t k, int sorted_
  * Returns ORACLE_OK, ORACLE_BAD_ARG, ORACLE_NAN (some row holds a NaN in
  * [0, n); outputs are then incomplete) or ORACLE_NOMEM.
  */
+int oracle_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
+                        int32_t k, const int32_t* lengths, int sorted_index, int return_value,
+                        int32_t* out_idx, void* out_val, int nthreads);
+
 int oracle_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
                 int32_t k, int sorted_index, int return_value, int32_t* out_idx,
                 void* out_val, int nthreads) {
+    return oracle_topk_lengths(in, dtype, batch, n, row_stride, k, NULL, sorted_index, return_value,
+                               out_idx, out_val, nthreads);
+}
+
+/*
+ * As oracle_topk, with row r's valid columns [0, lengths[r]) (host array of
+ * batch entries, each clamped to [0, n]; NULL: all n valid).
+ */
+int oracle_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
+                        int32_t k, const int32_t* lengths, int sorted_index, int return_value,
+                        int32_t* out_idx, void* out_val, int nthreads) {
     if ((dtype != ORACLE_BF16 && dtype != ORACLE_F32) || sorted_index < 0 || sorted_index > 2 || batch < 0 || n < 1 || k < 1 ||
         k > n || row_stride < n || !in || !out_idx || (return_value && !out_val))
         return ORACLE_BAD_ARG;
@@ -135,7 +162,9 @@ int oracle_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row
 #endif
     for (int64_t r = 0; r < batch; ++r) {
         const void* row = (const char*)in + es * (size_t)(r * row_stride);
-        int s = one_row(row, dtype, n, k, sorted_index, return_value, out_idx + r * (int64_t)k,
+        int64_t len = lengths ? (int64_t)lengths[r] : n;
+        len = len < 0 ? 0 : len > n ? n : len;
+        int s = one_row(row, dtype, n, len, k, sorted_index, return_value, out_idx + r * (int64_t)k,
                         return_value ? (char*)out_val + es * (size_t)(r * (int64_t)k) : NULL);
         if (s > status) status = s;
     }

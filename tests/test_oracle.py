@@ -212,6 +212,56 @@ def test_value_order_is_rank_order(oracle_mod, dtype):
     assert oracle_mod.topk(make_edge_rows("f32", 1, 16, seed=0), "f32", 16, 4, sorted_index=3)[0] == oracle_mod.BAD_ARG
 
 
+def _neg_inf_tail(raw, dtype, lens):
+    # the rows as the lengths describe them: columns >= len hold -inf
+    t = raw.copy()
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for r, L in enumerate(lens):
+        t[r, max(0, min(L, t.shape[1])):] = ninf
+    return t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lengths_match_brute_force_on_neg_inf_tails(oracle_mod, dtype):
+    # Row r with valid length L is the row whose columns >= L are -inf: the
+    # selected set is checked against brute-force ranks of that row, the value
+    # order position by position, and the tail's values are -inf bit patterns.
+    rng = np.random.default_rng(7)
+    for trial in range(8):
+        n = int(rng.integers(20, 90))
+        raw = make_edge_rows(dtype, 4, n, seed=200 + trial, levels=4 if trial % 2 else 0, specials=0.05)
+        lens = [0, int(rng.integers(1, n)), n, n + 5][: raw.shape[0]]
+        filled = _neg_inf_tail(raw, dtype, lens)
+        for k in (1, 5, n):
+            st, idx, val = oracle_mod.topk_lengths(raw, dtype, n, k, lens, sorted_index=2)
+            assert st == 0
+            for r in range(raw.shape[0]):
+                row = filled[r, :n]
+                assert sorted(idx[r].tolist()) == topk_set_loop(row, dtype, k)
+                vals = brute.decode(row, dtype)
+                ranks = [sum(1 for j in range(n) if j != i and brute.precedes(vals[j], j, vals[i], i))
+                         for i in range(n)]
+                assert idx[r].tolist() == sorted(range(n), key=lambda i: ranks[i])[:k]
+                want = filled[r, idx[r]]
+                assert np.array_equal(val[r].view(np.uint16 if dtype == "bf16" else np.uint32),
+                                      want.view(np.uint16 if dtype == "bf16" else np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lengths_never_read_the_tail(oracle_mod, dtype):
+    # NaN past a row's length is not looked at; NaN inside it is reported.
+    n = 64
+    raw = make_edge_rows(dtype, 2, n, seed=5)
+    nan = np.uint16(0x7FC1) if dtype == "bf16" else np.float32(np.nan)
+    raw[:, 40:] = nan
+    st, idx, _ = oracle_mod.topk_lengths(raw, dtype, n, 8, [40, 12], sorted_index=1)
+    assert st == 0
+    assert oracle_mod.topk_lengths(raw, dtype, n, 8, [41, 12], sorted_index=1)[0] == oracle_mod.NAN
+    # a length below k: the valid columns, then the first tail columns
+    st, idx, val = oracle_mod.topk_lengths(raw, dtype, n, 8, [3, 0], sorted_index=1)
+    assert st == 0 and idx[0].tolist() == list(range(8)) and idx[1].tolist() == list(range(8))
+
+
 # ---------------------------------------------------------------- planted mistakes
 _MUTANTS = {
     "tie_to_higher_index": ("if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
@@ -221,6 +271,8 @@ _MUTANTS = {
     "bf16_low_half": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b;"),
     "no_nan_check": ("if (isnan(it[c].v)) {", "if (0) {"),
     "value_order_by_index": ("if (sorted_index == 1) qsort", "if (sorted_index) qsort"),
+    "lengths_read_tail": ("it[c].v = c < len ? widen(row, dtype, c) : -INFINITY;", "it[c].v = widen(row, dtype, c);"),
+    "lengths_off_by_one": ("it[c].v = c < len ? widen", "it[c].v = c <= len ? widen"),
 }
 
 
@@ -244,6 +296,8 @@ def _pins_pass(oracle_mod):
         test_nan_status(oracle_mod, "bf16")
         test_nan_status(oracle_mod, "f32")
         test_value_order_is_rank_order(oracle_mod, "bf16")
+        test_lengths_match_brute_force_on_neg_inf_tails(oracle_mod, "f32")
+        test_lengths_never_read_the_tail(oracle_mod, "bf16")
     except AssertionError:
         return False
     return True
@@ -257,5 +311,7 @@ def test_planted_mistake_is_caught(oracle_mod, name, monkeypatch):
     lib = ctypes.CDLL(so)
     lib.oracle_topk.restype = ctypes.c_int
     lib.oracle_topk.argtypes = oracle_mod._load().oracle_topk.argtypes
+    lib.oracle_topk_lengths.restype = ctypes.c_int
+    lib.oracle_topk_lengths.argtypes = oracle_mod._load().oracle_topk_lengths.argtypes
     monkeypatch.setattr(oracle_mod, "_lib", lib)
     assert not _pins_pass(oracle_mod), "pins did not catch mutant %s" % name
