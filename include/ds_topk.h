@@ -141,6 +141,27 @@ int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t r
                   int32_t k, int sorted_index, int return_value, int32_t* out_idx, void* out_val,
                   int32_t* status_dev, void* stream);
 
+/*
+ * ds_topk_lengths: ds_topk with a valid length per row, in place of -inf
+ * tails (a decode-time indexer row covers a context of its own length; the
+ * aiutil card, 关键技术亮点 item 1, gives the indexer's vocab range as
+ * 1~+∞).
+ *
+ * Arguments are those of ds_topk, plus `lengths`: a device pointer to batch
+ * int32 values; row r's valid columns are [0, lengths[r]), a length outside
+ * [0, n] being clamped to it.  Columns past a row's length act as -inf: they
+ * are not read (beyond the 16-byte vector holding the row's last valid
+ * column), never NaN-checked, and rank after every valid column; when
+ * a row is shorter than k its output ends with those columns, lowest index
+ * first, with -inf values (bit pattern 0xFF80 / 0xFF800000).  The result
+ * equals ds_topk on the same rows with their tails set to -inf.  A null
+ * `lengths` (with batch > 0) is DS_ERR_INVALID_ARGUMENT; the lengths
+ * themselves are not validated on the host.  Synchronous, like ds_topk.
+ */
+int ds_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                    const int32_t* lengths, int sorted_index, int return_value, int32_t* out_idx,
+                    void* out_val, void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* ds_topk_status_string(int status);
 

@@ -40,7 +40,7 @@ DS_ORDER_VALUE = 2
 
 MAX_K = 4096
 
-EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_status_string", "ds_topk_last_error",
+EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_status_string", "ds_topk_last_error",
            "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_version")
 
 
@@ -75,6 +75,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp]
     lib.ds_topk_async.restype = ci
     lib.ds_topk_async.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp, vp]
+    lib.ds_topk_lengths.restype = ci
+    lib.ds_topk_lengths.argtypes = [vp, ci, i64, i64, i64, i32, vp, ci, ci, vp, vp, vp]
     lib.ds_topk_status_string.restype = ctypes.c_char_p
     lib.ds_topk_status_string.argtypes = [ci]
     lib.ds_topk_last_error.restype = ctypes.c_char_p
@@ -95,6 +97,13 @@ def ds_topk(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int
             return_value: int, out_idx_ptr: int, out_val_ptr: Optional[int], stream: Optional[int]) -> int:
     return load_library().ds_topk(in_ptr, dtype, batch, n, row_stride, k, sorted_index, return_value,
                                   out_idx_ptr, out_val_ptr, stream)
+
+
+def ds_topk_lengths(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int,
+                    lengths_ptr: Optional[int], sorted_index: int, return_value: int, out_idx_ptr: int,
+                    out_val_ptr: Optional[int], stream: Optional[int]) -> int:
+    return load_library().ds_topk_lengths(in_ptr, dtype, batch, n, row_stride, k, lengths_ptr, sorted_index,
+                                          return_value, out_idx_ptr, out_val_ptr, stream)
 
 
 def ds_topk_async(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, sorted_index: int,
@@ -168,23 +177,33 @@ def _order(sorted_index: bool, sorted_value: bool) -> int:
 
 
 def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: bool = True,
-         n: Optional[int] = None, sorted_value: bool = False) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+         n: Optional[int] = None, sorted_value: bool = False, lengths: Optional[torch.Tensor] = None
+         ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """Top-k of each row of ``x`` ([batch, n], bf16 or fp32, on the device).
 
     Returns ``(values, indices)``; values is None when ``return_value`` is
     False.  Indices are int32.  ``sorted_index`` writes each row's indices in
     ascending order, ``sorted_value`` largest value first (ties by lower
     index); neither leaves the order free.  ``n`` restricts the selection to
-    the first n columns (the rest of each row is padding).  Blocks until
-    done.
+    the first n columns (the rest of each row is padding).  ``lengths`` (an
+    int32 device tensor, one per row) gives each row's own valid length: the
+    columns past it act as -inf and are not read.  Blocks until done.
     """
     order = _order(sorted_index, sorted_value)
     x, dt, batch, n, row_stride = _marshal(x, k, n)
     idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
     val = torch.empty((batch, k), dtype=x.dtype, device=x.device) if return_value else None
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = ds_topk(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)),
-                 idx.data_ptr(), val.data_ptr() if val is not None else None, stream)
+    if lengths is not None:
+        if lengths.dtype != torch.int32 or not lengths.is_cuda or lengths.numel() != batch or \
+                not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous int32 device tensor with one entry per row")
+        st = ds_topk_lengths(x.data_ptr(), dt, batch, n, row_stride, k, lengths.data_ptr(), order,
+                             int(bool(return_value)), idx.data_ptr(), val.data_ptr() if val is not None else None,
+                             stream)
+    else:
+        st = ds_topk(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)),
+                     idx.data_ptr(), val.data_ptr() if val is not None else None, stream)
     _check(st)
     return val, idx
 

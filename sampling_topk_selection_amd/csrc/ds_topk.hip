@@ -224,7 +224,8 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
 }
 
 int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
-        int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream) {
+        int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream,
+        const int32_t* lengths = nullptr) {
     g_err.clear();
     int st = validate(dtype, batch, n, row_stride, k);
     if (st) return st;
@@ -282,6 +283,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.flag = flag;
         prm.flag_value = flag_value;
         prm.flags = g_flags.load();
+        prm.lengths = lengths ? lengths + r0 : nullptr;
         e = launch(pl, prm, rows, stream);
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
     }
@@ -311,6 +313,13 @@ int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t r
     if (!status_dev) return fail(DS_ERR_INVALID_ARGUMENT, "status_dev is NULL");
     return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, status_dev,
                (hipStream_t)stream);
+}
+int ds_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                    const int32_t* lengths, int sorted_index, int return_value, int32_t* out_idx, void* out_val,
+                    void* stream) {
+    if (!lengths && batch > 0) return fail(DS_ERR_INVALID_ARGUMENT, "lengths is NULL");
+    return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, nullptr,
+               (hipStream_t)stream, lengths);
 }
 
 const char* ds_topk_status_string(int status) {

@@ -1538,7 +1538,21 @@ struct Params {
     int32_t* flag;     // set to flag_value when a NaN is seen
     int32_t flag_value;
     int32_t flags;     // kFlag* bits
+    const int32_t* lengths;  // [batch] valid columns per row (clamped to [0, n]), or null: all n
 };
+
+// Output slots [k, kout) of a row with only k = len < kout valid columns:
+// the columns len .. kout - 1, which act as -inf (they come after every
+// valid entry in each order), with -inf values.
+template <class E, int WG>
+__device__ __forceinline__ void write_tail(int32_t* row_idx, void* row_val, u32 k, u32 kout) {
+    using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
+    constexpr VT kNegInf = E::kKeyBits == 16 ? (VT)0xFF80u : (VT)0xFF800000u;
+    for (u32 j = k + threadIdx.x; j < kout; j += WG) {
+        row_idx[j] = (int32_t)j;
+        if (row_val) ((VT*)row_val)[j] = kNegInf;
+    }
+}
 
 __device__ __forceinline__ u32 hash32(u32 x) {
     x ^= x >> 16;
@@ -1674,12 +1688,28 @@ void topk_rows(Params p) {
     const u32 tid = threadIdx.x;
     const u32 row = blockIdx.x / (u32)p.segs;
     const u32 seg = blockIdx.x % (u32)p.segs;
-    const u32 k = (u32)p.k;
-    const u32 n = (u32)p.n;
+    // n: the row's valid columns; k: entries selected from them (k < kout
+    // only for a row shorter than the output, whose other slots are the -inf
+    // columns past its end)
+    const u32 kout = (u32)p.k;
+    u32 n = (u32)p.n;
+    if (p.lengths) {
+        const int32_t len = p.lengths[row];
+        n = len < 0 ? 0u : (u32)len < n ? (u32)len : n;
+    }
+    const u32 k = kout < n ? kout : n;
     const uint8_t* row_in = p.in + (int64_t)row * p.row_stride_bytes;
+    int32_t* const row_idx = p.out_idx + (int64_t)row * kout;
+    void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * kout * EB) : nullptr;
+    if (k == 0) {  // no valid column: the whole output is the -inf columns
+        if (seg == 0) write_tail<E, WG>(row_idx, row_val, 0u, kout);
+        return;
+    }
 
     const int v0 = (int)seg * p.seg_vecs;
-    const int v1 = min(p.n_vec, v0 + p.seg_vecs);
+    int v1 = min(p.n_vec, v0 + p.seg_vecs);
+    v1 = min(v1, (int)((n + E::kPerVec - 1) / E::kPerVec));  // vectors with valid columns
+    v1 = max(v1, v0);
     // The segment as a raw buffer resource: loads take one 32-bit offset
     // (vector index relative to v0, times 16) and the hardware range check
     // returns zeros past the segment's end instead of faulting.
@@ -1852,14 +1882,13 @@ void topk_rows(Params p) {
     DSTK_PHASE(9);
     u32 cnt = sm.count;
     const u32 wave = tid / kWave;
-    int32_t* const row_idx = p.out_idx + (int64_t)row * k;
-    void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * k * EB) : nullptr;
 
     if (p.segs == 1) {
         block_locate<WG, CAP>(sm, k, 0u, true);
         DSTK_PHASE(2);
         select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, n, p.sorted, p.retval,
                                     p.flags, row_idx, row_val, p.flag, p.flag_value);
+        if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
         DSTK_PHASE(6);
         DSTK_PROBE_FLUSH();
         return;
@@ -2055,6 +2084,7 @@ void topk_rows(Params p) {
         merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
                                    p.sorted, p.retval,
                                    p.flags, row_idx, row_val, p.flag, p.flag_value);
+        if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
         return;
     }
     {
@@ -2086,6 +2116,7 @@ void topk_rows(Params p) {
     DSTK_PHASE(14);
     select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, n, p.sorted, p.retval, p.flags, row_idx, row_val, p.flag,
                                 p.flag_value);
+    if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
     DSTK_PHASE(6);
     DSTK_PROBE_FLUSH();
 }
