@@ -162,6 +162,29 @@ int ds_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t
                     const int32_t* lengths, int sorted_index, int return_value, int32_t* out_idx,
                     void* out_val, void* stream);
 
+/*
+ * ds_topk_ex: every option in one call.  Arguments as ds_topk, except that
+ * out_idx is untyped (its element type is set by the options) and `opt`
+ * (may be NULL: all defaults) adds:
+ *   index_bytes  4 (int32 indices; also 0) or 8 (int64: the usage example on
+ *                the CSDN page, section 三, passes indices_type=torch.int32,
+ *                one choice of an index type); other values are
+ *                DS_ERR_INVALID_ARGUMENT.
+ *   lengths      NULL, or per-row valid lengths as in ds_topk_lengths.
+ *   status_dev   NULL: synchronous, as ds_topk.  Else: enqueue only, NaN
+ *                reported into *status_dev, as ds_topk_async.
+ * The caller owns the options struct; it is read during the call only.
+ */
+typedef struct ds_topk_options {
+    int32_t index_bytes;
+    const int32_t* lengths;
+    int32_t* status_dev;
+} ds_topk_options;
+
+int ds_topk_ex(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+               int sorted_index, int return_value, void* out_idx, void* out_val, const ds_topk_options* opt,
+               void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* ds_topk_status_string(int status);
 

@@ -40,7 +40,7 @@ DS_ORDER_VALUE = 2
 
 MAX_K = 4096
 
-EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_status_string", "ds_topk_last_error",
+EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_ex", "ds_topk_status_string", "ds_topk_last_error",
            "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_version")
 
 
@@ -55,6 +55,10 @@ class ds_topk_plan(ctypes.Structure):
                 ("tiles_per_chunk", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("segment_vectors", ctypes.c_int32), ("tiles_per_segment", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+class ds_topk_options(ctypes.Structure):
+    _fields_ = [("index_bytes", ctypes.c_int32), ("lengths", ctypes.c_void_p), ("status_dev", ctypes.c_void_p)]
 
 
 _lib = None
@@ -77,6 +81,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk_async.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp, vp]
     lib.ds_topk_lengths.restype = ci
     lib.ds_topk_lengths.argtypes = [vp, ci, i64, i64, i64, i32, vp, ci, ci, vp, vp, vp]
+    lib.ds_topk_ex.restype = ci
+    lib.ds_topk_ex.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, ctypes.POINTER(ds_topk_options), vp]
     lib.ds_topk_status_string.restype = ctypes.c_char_p
     lib.ds_topk_status_string.argtypes = [ci]
     lib.ds_topk_last_error.restype = ctypes.c_char_p
@@ -104,6 +110,15 @@ def ds_topk_lengths(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int
                     out_val_ptr: Optional[int], stream: Optional[int]) -> int:
     return load_library().ds_topk_lengths(in_ptr, dtype, batch, n, row_stride, k, lengths_ptr, sorted_index,
                                           return_value, out_idx_ptr, out_val_ptr, stream)
+
+
+def ds_topk_ex(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, sorted_index: int,
+               return_value: int, out_idx_ptr: int, out_val_ptr: Optional[int], index_bytes: int = 4,
+               lengths_ptr: Optional[int] = None, status_dev_ptr: Optional[int] = None,
+               stream: Optional[int] = None) -> int:
+    opt = ds_topk_options(index_bytes, lengths_ptr, status_dev_ptr)
+    return load_library().ds_topk_ex(in_ptr, dtype, batch, n, row_stride, k, sorted_index, return_value,
+                                     out_idx_ptr, out_val_ptr, ctypes.byref(opt), stream)
 
 
 def ds_topk_async(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, sorted_index: int,
@@ -176,9 +191,21 @@ def _order(sorted_index: bool, sorted_value: bool) -> int:
     return DS_ORDER_VALUE if sorted_value else DS_ORDER_INDEX if sorted_index else DS_ORDER_NONE
 
 
+_INDEX_BYTES = {torch.int32: 4, torch.int64: 8}
+
+
+def _lengths_ptr(lengths: Optional[torch.Tensor], batch: int) -> Optional[int]:
+    if lengths is None:
+        return None
+    if lengths.dtype != torch.int32 or not lengths.is_cuda or lengths.numel() != batch or \
+            not lengths.is_contiguous():
+        raise ValueError("lengths must be a contiguous int32 device tensor with one entry per row")
+    return lengths.data_ptr()
+
+
 def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: bool = True,
-         n: Optional[int] = None, sorted_value: bool = False, lengths: Optional[torch.Tensor] = None
-         ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+         n: Optional[int] = None, sorted_value: bool = False, lengths: Optional[torch.Tensor] = None,
+         indices_type: torch.dtype = torch.int32) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """Top-k of each row of ``x`` ([batch, n], bf16 or fp32, on the device).
 
     Returns ``(values, indices)``; values is None when ``return_value`` is
@@ -187,20 +214,20 @@ def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: b
     index); neither leaves the order free.  ``n`` restricts the selection to
     the first n columns (the rest of each row is padding).  ``lengths`` (an
     int32 device tensor, one per row) gives each row's own valid length: the
-    columns past it act as -inf and are not read.  Blocks until done.
+    columns past it act as -inf and are not read.  ``indices_type`` is
+    torch.int32 or torch.int64.  Blocks until done.
     """
     order = _order(sorted_index, sorted_value)
+    if indices_type not in _INDEX_BYTES:
+        raise ValueError("indices_type must be torch.int32 or torch.int64")
     x, dt, batch, n, row_stride = _marshal(x, k, n)
-    idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+    idx = torch.empty((batch, k), dtype=indices_type, device=x.device)
     val = torch.empty((batch, k), dtype=x.dtype, device=x.device) if return_value else None
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    if lengths is not None:
-        if lengths.dtype != torch.int32 or not lengths.is_cuda or lengths.numel() != batch or \
-                not lengths.is_contiguous():
-            raise ValueError("lengths must be a contiguous int32 device tensor with one entry per row")
-        st = ds_topk_lengths(x.data_ptr(), dt, batch, n, row_stride, k, lengths.data_ptr(), order,
-                             int(bool(return_value)), idx.data_ptr(), val.data_ptr() if val is not None else None,
-                             stream)
+    if lengths is not None or indices_type != torch.int32:
+        st = ds_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)), idx.data_ptr(),
+                        val.data_ptr() if val is not None else None, _INDEX_BYTES[indices_type],
+                        _lengths_ptr(lengths, batch), None, stream)
     else:
         st = ds_topk(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)),
                      idx.data_ptr(), val.data_ptr() if val is not None else None, stream)
@@ -210,25 +237,34 @@ def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: b
 
 def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: bool = False,
                return_value: bool = True, n: Optional[int] = None,
-               out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor]] = None, sorted_value: bool = False
+               out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor]] = None, sorted_value: bool = False,
+               lengths: Optional[torch.Tensor] = None, indices_type: torch.dtype = torch.int32
                ) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
     """Enqueue the selection on the current stream without waiting.
 
     ``status`` is a zero-initialised int32 device tensor (one element); the
     kernels store DS_ERR_NAN there if a row holds NaN.  ``out`` may supply
-    preallocated (values, indices).  Order arguments as for topk()."""
+    preallocated (values, indices).  Other arguments as for topk()."""
     order = _order(sorted_index, sorted_value)
     x, dt, batch, n, row_stride = _marshal(x, k, n)
     if out is not None:
         val, idx = out
+        indices_type = idx.dtype
     else:
-        idx = torch.empty((batch, k), dtype=torch.int32, device=x.device)
+        idx = torch.empty((batch, k), dtype=indices_type, device=x.device)
         val = torch.empty((batch, k), dtype=x.dtype, device=x.device) if return_value else None
+    if indices_type not in _INDEX_BYTES:
+        raise ValueError("indices must be torch.int32 or torch.int64")
     if status.dtype != torch.int32 or not status.is_cuda:
         raise ValueError("status must be an int32 device tensor")
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = ds_topk_async(x.data_ptr(), dt, batch, n, row_stride, k, order,
-                       int(bool(return_value)), idx.data_ptr(), val.data_ptr() if val is not None else None,
-                       status.data_ptr(), stream)
+    if lengths is not None or indices_type != torch.int32:
+        st = ds_topk_ex(x.data_ptr(), dt, batch, n, row_stride, k, order, int(bool(return_value)), idx.data_ptr(),
+                        val.data_ptr() if val is not None else None, _INDEX_BYTES[indices_type],
+                        _lengths_ptr(lengths, batch), status.data_ptr(), stream)
+    else:
+        st = ds_topk_async(x.data_ptr(), dt, batch, n, row_stride, k, order,
+                           int(bool(return_value)), idx.data_ptr(), val.data_ptr() if val is not None else None,
+                           status.data_ptr(), stream)
     _check(st)
     return val, idx

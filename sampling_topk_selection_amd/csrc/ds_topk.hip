@@ -224,13 +224,15 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
 }
 
 int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
-        int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream,
-        const int32_t* lengths = nullptr) {
+        int return_value, void* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream,
+        const int32_t* lengths = nullptr, int index_bytes = 4) {
     g_err.clear();
     int st = validate(dtype, batch, n, row_stride, k);
     if (st) return st;
     if (sorted_index < DS_ORDER_NONE || sorted_index > DS_ORDER_VALUE)
         return fail(DS_ERR_INVALID_ARGUMENT, "sorted_index %d is not a ds_topk_order", sorted_index);
+    if (index_bytes != 4 && index_bytes != 8)
+        return fail(DS_ERR_INVALID_ARGUMENT, "index_bytes %d is neither 4 nor 8", index_bytes);
     if (!in) return fail(DS_ERR_INVALID_ARGUMENT, "in is NULL");
     if (!out_idx) return fail(DS_ERR_INVALID_ARGUMENT, "out_idx is NULL");
     if (return_value && !out_val) return fail(DS_ERR_INVALID_ARGUMENT, "return_value set but out_val is NULL");
@@ -273,7 +275,8 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.seed = g_tile_seed.load();
         prm.sorted = sorted_index;
         prm.retval = return_value ? 1 : 0;
-        prm.out_idx = out_idx + r0 * k;
+        prm.out_idx = (uint8_t*)out_idx + r0 * k * index_bytes;
+        prm.idx64 = index_bytes == 8 ? 1 : 0;
         prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
         prm.ws_cand = ws->cand;
         prm.ws_meta = ws->meta;
@@ -320,6 +323,14 @@ int ds_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t
     if (!lengths && batch > 0) return fail(DS_ERR_INVALID_ARGUMENT, "lengths is NULL");
     return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, nullptr,
                (hipStream_t)stream, lengths);
+}
+int ds_topk_ex(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+               int return_value, void* out_idx, void* out_val, const ds_topk_options* opt, void* stream) {
+    ds_topk_options o{};
+    if (opt) o = *opt;
+    const int ib = o.index_bytes == 0 ? 4 : o.index_bytes;
+    return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, o.status_dev,
+               (hipStream_t)stream, o.lengths, ib);
 }
 
 const char* ds_topk_status_string(int status) {

@@ -163,6 +163,21 @@ constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index 
 constexpr int kOrderIndex = 1;   // Params::sorted: ascending column index
 constexpr int kOrderValue = 2;   // Params::sorted: largest composite first
 
+// Where a row's column indices go: int32 or int64 elements.
+struct IdxOut {
+    void* p;
+    int i64;
+    __device__ __forceinline__ void put(u32 pos, u32 col) const {
+        if (i64)
+            ((int64_t*)p)[pos] = (int64_t)col;
+        else
+            ((int32_t*)p)[pos] = (int32_t)col;
+    }
+    __device__ __forceinline__ IdxOut at(u64 pos) const {
+        return IdxOut{(void*)((uint8_t*)p + pos * (i64 ? 8u : 4u)), i64};
+    }
+};
+
 // Histogram storage is transposed with a padded row: bin d lives at
 // ((d mod 32) * 65 + d / 32), so atomics on consecutive bins (the hot bins
 // next to the bound) and reads of runs of bins by consecutive lanes hit
@@ -752,7 +767,7 @@ struct ColRanks {
 // fits in the free LDS), else from a bitonic sort; value order from a
 // bitonic sort of the composites.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, int32_t* out_idx,
+__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, IdxOut out_idx,
                      void* out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
@@ -760,7 +775,7 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
     if (!sorted) {
         for (u32 i = tid; i < k; i += WG) {
             const u64 e = sm.buf[i];
-            out_idx[i] = (int32_t)comp_col<E>(e);
+            out_idx.put(i, comp_col<E>(e));
             if (retval) ov[i] = (VT)E::bits(comp_key<E>(e));
         }
         return;
@@ -780,7 +795,7 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
             const u64 e = sm.buf[i];
             const u32 c = comp_col<E>(e);
             const u32 pos = cr.rank(c, sm.tbase);
-            out_idx[pos] = (int32_t)c;
+            out_idx.put(pos, c);
             if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
         }
         return;
@@ -813,10 +828,10 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
     for (u32 i = tid; i < k; i += WG) {
         const u64 s = sm.buf[i];
         if (sorted == kOrderValue) {
-            out_idx[i] = (int32_t)comp_col<E>(~s);
+            out_idx.put(i, comp_col<E>(~s));
             if (retval) ov[i] = (VT)E::bits(comp_key<E>(~s));
         } else {
-            out_idx[i] = (int32_t)(u32)(s >> 32);
+            out_idx.put(i, (u32)(s >> 32));
             if (retval) ov[i] = (VT)E::bits((u32)s);
         }
     }
@@ -1103,7 +1118,7 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
 // order by a bitmap behind them, or a bitonic sort).
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
-                                            int flags, int32_t* out_idx, void* out_val) {
+                                            int flags, IdxOut out_idx, void* out_val) {
     __syncthreads();
     keep_at_least<WG, CAP>(sm, 0, cnt, T);
     emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx, out_val);
@@ -1134,7 +1149,7 @@ __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u3
 // when no bitmap fits, compact and fall back to emit().
 template <class E, int WG, int CAP>
 __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
-                                               int flags, int32_t* out_idx, void* out_val) {
+                                               int flags, IdxOut out_idx, void* out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
     VT* ov = (VT*)out_val;
@@ -1147,7 +1162,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
             const u64 e = sm.buf[i];
             if (e >= T) {
                 if (pos < k) {
-                    out_idx[pos] = (int32_t)comp_col<E>(e);
+                    out_idx.put(pos, comp_col<E>(e));
                     if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
                 }
                 ++pos;
@@ -1187,7 +1202,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
             const u32 c = comp_col<E>(e);
             const u32 pos = cr.rank(c, sm.tbase);
             if (pos < k) {
-                out_idx[pos] = (int32_t)c;
+                out_idx.put(pos, c);
                 if (retval) ov[pos] = (VT)E::bits(comp_key<E>(e));
             }
         }
@@ -1528,7 +1543,8 @@ struct Params {
     uint32_t seed;
     int32_t sorted;    // output order: 0, kOrderIndex or kOrderValue
     int32_t retval;
-    int32_t* out_idx;
+    void* out_idx;     // [batch][k] int32, or int64 with idx64
+    int32_t idx64;
     void* out_val;
     u64* ws_cand;      // [batch][segs][pub_cap]: a segment's live candidates, by top digit
     u64* ws_meta;      // [batch][segs][4]: count | low digit, high digit, bound, q-bound
@@ -1545,11 +1561,11 @@ struct Params {
 // the columns len .. kout - 1, which act as -inf (they come after every
 // valid entry in each order), with -inf values.
 template <class E, int WG>
-__device__ __forceinline__ void write_tail(int32_t* row_idx, void* row_val, u32 k, u32 kout) {
+__device__ __forceinline__ void write_tail(IdxOut row_idx, void* row_val, u32 k, u32 kout) {
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
     constexpr VT kNegInf = E::kKeyBits == 16 ? (VT)0xFF80u : (VT)0xFF800000u;
     for (u32 j = k + threadIdx.x; j < kout; j += WG) {
-        row_idx[j] = (int32_t)j;
+        row_idx.put(j, j);
         if (row_val) ((VT*)row_val)[j] = kNegInf;
     }
 }
@@ -1594,7 +1610,7 @@ struct Slot {
 // rank r1 of c1 inside it) and output; then the NaN report.
 template <class E, int WG, int CAP>
 __device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 n, int sorted,
-                                             int retval, int flags, int32_t* row_idx, void* row_val, int32_t* flag,
+                                             int retval, int flags, IdxOut row_idx, void* row_val, int32_t* flag,
                                              int32_t flag_value) {
     const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
     DSTK_PHASE(5);
@@ -1609,7 +1625,7 @@ __device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32
 template <class E, int WG, int CAP>
 __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, const u32* rdir, const u64* rc, u32 S,
                                             u32 cap, u64 Lrow, u32 k, u32 n, int sorted, int retval, int flags,
-                                            int32_t* row_idx, void* row_val, int32_t* flag, int32_t flag_value) {
+                                            IdxOut row_idx, void* row_val, int32_t* flag, int32_t flag_value) {
     const u32 tid = threadIdx.x;
     const u32 dL = top_digit(Lrow);
     constexpr int kMI = E::kPerVec;  // entries per thread per step (one tile's worth)
@@ -1699,7 +1715,7 @@ void topk_rows(Params p) {
     }
     const u32 k = kout < n ? kout : n;
     const uint8_t* row_in = p.in + (int64_t)row * p.row_stride_bytes;
-    int32_t* const row_idx = p.out_idx + (int64_t)row * kout;
+    const IdxOut row_idx = IdxOut{p.out_idx, p.idx64}.at((u64)row * kout);
     void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * kout * EB) : nullptr;
     if (k == 0) {  // no valid column: the whole output is the -inf columns
         if (seg == 0) write_tail<E, WG>(row_idx, row_val, 0u, kout);
