@@ -276,7 +276,6 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.sorted = sorted_index;
         prm.retval = return_value ? 1 : 0;
         prm.out_idx = (uint8_t*)out_idx + r0 * k * index_bytes;
-        prm.idx64 = index_bytes == 8 ? 1 : 0;
         prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
         prm.ws_cand = ws->cand;
         prm.ws_meta = ws->meta;
@@ -285,7 +284,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.ws_ticket = ws->ticket;
         prm.flag = flag;
         prm.flag_value = flag_value;
-        prm.flags = g_flags.load();
+        prm.flags = (g_flags.load() & dstk::kFlagBitonic) | (index_bytes == 8 ? dstk::kFlagIdx64 : 0);
         prm.lengths = lengths ? lengths + r0 : nullptr;
         e = launch(pl, prm, rows, stream);
         if (e != hipSuccess) return hip_fail(e, "kernel launch");

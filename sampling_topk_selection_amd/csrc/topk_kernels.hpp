@@ -160,6 +160,7 @@ __device__ __forceinline__ bool nan_slot(Elem<2>, const u32 (&dw)[4]) {
 constexpr int kHistBits = 11;  // radix-select digit width
 constexpr int kBins = 1 << kHistBits;
 constexpr int kFlagBitonic = 1;  // Params::flags: always use the bitonic index sort
+constexpr int kFlagIdx64 = 2;    // Params::flags: the output indices are int64
 constexpr int kOrderIndex = 1;   // Params::sorted: ascending column index
 constexpr int kOrderValue = 2;   // Params::sorted: largest composite first
 
@@ -767,8 +768,9 @@ struct ColRanks {
 // fits in the free LDS), else from a bitonic sort; value order from a
 // bitonic sort of the composites.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, IdxOut out_idx,
+__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, void* out_idx_p,
                      void* out_val) {
+    const IdxOut out_idx{out_idx_p, flags & kFlagIdx64};
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
     VT* ov = (VT*)out_val;
@@ -1118,10 +1120,11 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
 // order by a bitmap behind them, or a bitonic sort).
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
-                                            int flags, IdxOut out_idx, void* out_val) {
+                                            int flags, void* out_idx_p, void* out_val) {
+    const IdxOut out_idx{out_idx_p, flags & kFlagIdx64};
     __syncthreads();
     keep_at_least<WG, CAP>(sm, 0, cnt, T);
-    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx, out_val);
+    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx.p, out_val);
 }
 
 // Reduce buf[0, cnt) exactly to its k largest (b1/r1/c1 locate the k-th in
@@ -1179,7 +1182,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
         else if ((u64)cnt * 2 + need <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
     }
     if (!bm) {
-        emit_compacted<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, out_idx, out_val);
+        emit_compacted<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, out_idx.p, out_val);
         return;
     }
     const ColRanks<WG> cr(bm, lp, pitch);
@@ -1543,8 +1546,7 @@ struct Params {
     uint32_t seed;
     int32_t sorted;    // output order: 0, kOrderIndex or kOrderValue
     int32_t retval;
-    void* out_idx;     // [batch][k] int32, or int64 with idx64
-    int32_t idx64;
+    void* out_idx;     // [batch][k] int32, or int64 with kFlagIdx64
     void* out_val;
     u64* ws_cand;      // [batch][segs][pub_cap]: a segment's live candidates, by top digit
     u64* ws_meta;      // [batch][segs][4]: count | low digit, high digit, bound, q-bound
@@ -1610,8 +1612,9 @@ struct Slot {
 // rank r1 of c1 inside it) and output; then the NaN report.
 template <class E, int WG, int CAP>
 __device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 n, int sorted,
-                                             int retval, int flags, IdxOut row_idx, void* row_val, int32_t* flag,
+                                             int retval, int flags, void* row_idx_p, void* row_val, int32_t* flag,
                                              int32_t flag_value) {
+    const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
     DSTK_PHASE(5);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
@@ -1625,7 +1628,8 @@ __device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32
 template <class E, int WG, int CAP>
 __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, const u32* rdir, const u64* rc, u32 S,
                                             u32 cap, u64 Lrow, u32 k, u32 n, int sorted, int retval, int flags,
-                                            IdxOut row_idx, void* row_val, int32_t* flag, int32_t flag_value) {
+                                            void* row_idx_p, void* row_val, int32_t* flag, int32_t flag_value) {
+    const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u32 tid = threadIdx.x;
     const u32 dL = top_digit(Lrow);
     constexpr int kMI = E::kPerVec;  // entries per thread per step (one tile's worth)
@@ -1678,7 +1682,7 @@ __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, con
         if (c2 > (u32)(CAP - WG * kMI)) make_room<E, WG, CAP>(sm, c2, k, WG * kMI);
     }
     final_select<E, WG, CAP>(sm, sm.count, k);
-    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, row_idx, row_val);
+    emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, row_idx.p, row_val);
     __syncthreads();
     if (tid == 0 && sm.nan) *flag = flag_value;
 }
@@ -1715,7 +1719,7 @@ void topk_rows(Params p) {
     }
     const u32 k = kout < n ? kout : n;
     const uint8_t* row_in = p.in + (int64_t)row * p.row_stride_bytes;
-    const IdxOut row_idx = IdxOut{p.out_idx, p.idx64}.at((u64)row * kout);
+    const IdxOut row_idx = IdxOut{p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
     void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * kout * EB) : nullptr;
     if (k == 0) {  // no valid column: the whole output is the -inf columns
         if (seg == 0) write_tail<E, WG>(row_idx, row_val, 0u, kout);
@@ -1903,7 +1907,7 @@ void topk_rows(Params p) {
         block_locate<WG, CAP>(sm, k, 0u, true);
         DSTK_PHASE(2);
         select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, n, p.sorted, p.retval,
-                                    p.flags, row_idx, row_val, p.flag, p.flag_value);
+                                    p.flags, row_idx.p, row_val, p.flag, p.flag_value);
         if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
         DSTK_PHASE(6);
         DSTK_PROBE_FLUSH();
@@ -2099,7 +2103,7 @@ void topk_rows(Params p) {
     if (total > (u32)CAP) {
         merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
                                    p.sorted, p.retval,
-                                   p.flags, row_idx, row_val, p.flag, p.flag_value);
+                                   p.flags, row_idx.p, row_val, p.flag, p.flag_value);
         if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
         return;
     }
@@ -2130,7 +2134,8 @@ void topk_rows(Params p) {
     }
     __syncthreads();
     DSTK_PHASE(14);
-    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, n, p.sorted, p.retval, p.flags, row_idx, row_val, p.flag,
+    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, n, p.sorted, p.retval, p.flags, row_idx.p, row_val,
+                                p.flag,
                                 p.flag_value);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
     DSTK_PHASE(6);
