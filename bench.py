@@ -234,6 +234,34 @@ def main() -> int:
                 pkg.topk(x, w.k, sorted_index=w.sorted_index, return_value=w.return_value)
             per[cfg]["sync_call_us"] = round((time.perf_counter() - t) / r * 1e6, 1)
 
+    modes = {}
+    if not args.no_extras:
+        # the output-order and per-row-length modes, warm, back to back
+        def mode_us(x, w, reps=40, **kw):
+            st1 = torch.zeros(1, dtype=torch.int32, device=dev)
+            for _ in range(3):
+                pkg.topk_async(x, w.k, st1, n=w.n, **kw)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                pkg.topk_async(x, w.k, st1, n=w.n, **kw)
+            b.record(stream)
+            torch.cuda.synchronize()
+            assert int(st1.item()) == 0
+            return a.elapsed_time(b) * 1e3 / reps
+
+        w3 = W[DOMINANT]["w"]
+        x3 = W[DOMINANT]["x0"]
+        for name, kw in (("index", dict(sorted_index=True)), ("value", dict(sorted_value=True)),
+                         ("none", dict()), ("index_int64", dict(sorted_index=True, indices_type=torch.int64))):
+            modes["C3_order_%s_us" % name] = round(mode_us(x3, w3, return_value=True, **kw), 3)
+        w4 = make_workload("C4")
+        x4 = torch.from_numpy(np.ascontiguousarray(w4.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+        l4 = torch.tensor(w4.meta["lengths"], dtype=torch.int32, device=dev)
+        modes["C4_neg_inf_tails_us"] = round(mode_us(x4, w4, return_value=True), 3)
+        modes["C4_lengths_us"] = round(mode_us(x4, w4, return_value=True, lengths=l4), 3)
+        modes["C4_valid_bytes"] = int(sum(w4.meta["lengths"]) * 2 + w4.batch * w4.k * 6)
+
     if args.calib_copy:
         # a plain copy of the sampler input: known traffic for counter scaling
         d = W[DOMINANT]
@@ -348,6 +376,7 @@ def main() -> int:
             "cold_hbm": args.rotate_gb > 0,
             "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
             "per_workload": per,
+            "modes": modes,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
