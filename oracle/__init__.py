@@ -51,6 +51,10 @@ def _load():
         lib.oracle_topk_lengths.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_sample.restype = ctypes.c_int
+        lib.oracle_sample.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -102,3 +106,22 @@ def topk_lengths(raw: np.ndarray, dtype: str, n: int, k: int, lengths, sorted_in
                                  int(sorted_index), int(bool(return_value)), idx.ctypes.data,
                                  val.ctypes.data if val is not None else None, int(nthreads))
     return st, idx, val
+
+
+def sample(raw: np.ndarray, dtype: str, n: int, k: int, temperature, top_p, uniform
+           ) -> Tuple[int, np.ndarray]:
+    """One token per row drawn from the row's top-k (see oracle_sample in
+    oracle.c): temperature softmax over the candidates, top-p nucleus,
+    inverse CDF at the caller's uniform u.  Returns (status, int32 [batch])."""
+    lib = _load()
+    raw = np.ascontiguousarray(raw)
+    want = np.uint16 if dtype == "bf16" else np.float32
+    if raw.dtype != want:
+        raise TypeError("raw must be %s for %s" % (np.dtype(want).name, dtype))
+    batch, row_stride = raw.shape
+    f = [np.ascontiguousarray(np.broadcast_to(np.asarray(a, dtype=np.float32), (batch,)))
+         for a in (temperature, top_p, uniform)]
+    out = np.zeros(batch, dtype=np.int32)
+    st = lib.oracle_sample(raw.ctypes.data, _DT[dtype], batch, n, row_stride, k, f[0].ctypes.data,
+                           f[1].ctypes.data, f[2].ctypes.data, out.ctypes.data)
+    return st, out

@@ -172,6 +172,80 @@ int oracle_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int
     return status;
 }
 
+/*
+ * Sampling over the top-k candidates -- the step after the selection on the
+ * sampler path.  The pages name temperature and top-p as the generation
+ * parameters (CSDN page, section 二 接入层; zh-TW page, the deepseek-recipe
+ * section) without a formula; this is the textbook reading:
+ *   c_1 .. c_k   the row's top-k in value order (the order above);
+ *   w_j          exp((x_{c_j} - x_{c_1}) / T), with w_j = 1 where
+ *                x_{c_j} == x_{c_1} (equal values, +inf tops) and w_j = 0
+ *                where x_{c_j} = -inf below a larger top;
+ *   W_j          w_1 + ... + w_j;
+ *   m            the smallest j with W_j >= top_p * W_k (top-p nucleus;
+ *                at least one candidate; m = k when top_p >= 1);
+ *   token        c_j for the smallest j with W_j > u * W_m, u in [0, 1)
+ *                the caller's uniform draw (inverse CDF).
+ * T <= 0 (or NaN) means greedy: token = c_1.  u is clamped to [0, 1).
+ * Computed in double.  Returns as oracle_topk; out_token[r] per row.
+ */
+int oracle_sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                  const float* temperature, const float* top_p, const float* uniform, int32_t* out_token) {
+    if (!temperature || !top_p || !uniform || !out_token) return ORACLE_BAD_ARG;
+    if (batch <= 0) return batch < 0 ? ORACLE_BAD_ARG : ORACLE_OK;
+    int32_t* idx = (int32_t*)malloc((size_t)(batch * (int64_t)k) * sizeof(int32_t));
+    if (!idx) return ORACLE_NOMEM;
+    int st = oracle_topk(in, dtype, batch, n, row_stride, k, 2, 0, idx, NULL, 1);
+    if (st != ORACLE_OK) {
+        free(idx);
+        return st;
+    }
+    const size_t es = dtype == ORACLE_BF16 ? 2 : 4;
+    double* W = (double*)malloc((size_t)k * sizeof(double));
+    if (!W) {
+        free(idx);
+        return ORACLE_NOMEM;
+    }
+    for (int64_t r = 0; r < batch; ++r) {
+        const void* row = (const char*)in + es * (size_t)(r * row_stride);
+        const int32_t* c = idx + r * (int64_t)k;
+        const double T = temperature[r];
+        if (!(T > 0.0)) {
+            out_token[r] = c[0];
+            continue;
+        }
+        const double x1 = widen(row, dtype, c[0]);
+        double acc = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            const double x = widen(row, dtype, c[j]);
+            const double w = x == x1 ? 1.0 : isinf(x) && x < 0 ? 0.0 : exp((x - x1) / T);
+            acc += w;
+            W[j] = acc;
+        }
+        const double p = top_p[r];
+        int32_t m = k;  /* 1-based nucleus size */
+        for (int32_t j = 0; j < k; ++j)
+            if (W[j] >= p * W[k - 1]) {
+                m = j + 1;
+                break;
+            }
+        double u = uniform[r];
+        if (!(u >= 0.0)) u = 0.0;
+        if (u >= 1.0) u = nextafter(1.0, 0.0);
+        const double t = u * W[m - 1];
+        int32_t pick = m - 1;
+        for (int32_t j = 0; j < m; ++j)
+            if (W[j] > t) {
+                pick = j;
+                break;
+            }
+        out_token[r] = c[pick];
+    }
+    free(W);
+    free(idx);
+    return ORACLE_OK;
+}
+
 /* Number of threads a call with nthreads <= 0 would use. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

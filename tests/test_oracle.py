@@ -10,6 +10,7 @@ The oracle is checked against things other than itself:
   * planted mistakes: mutated copies of oracle.c must fail these pins.
 """
 
+import math
 import os
 import subprocess
 import tempfile
@@ -262,6 +263,97 @@ def test_lengths_never_read_the_tail(oracle_mod, dtype):
     assert st == 0 and idx[0].tolist() == list(range(8)) and idx[1].tolist() == list(range(8))
 
 
+# ---------------------------------------------------------------- sampling over the top-k
+def _row(dtype, vals, n=64, fill=-1000.0):
+    # one row: the given leading values, then a low fill
+    x = np.full((1, n), fill, dtype=np.float32)
+    x[0, : len(vals)] = vals
+    return bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sample_greedy_cases(oracle_mod, dtype):
+    # T <= 0, top_p = 0 and u = 0 all give the first candidate in value order
+    raw = make_edge_rows(dtype, 3, 500, seed=31)
+    st, top, _ = oracle_mod.topk(raw, dtype, 500, 1, 2, False)
+    for T, p, u in ((0.0, 1.0, 0.7), (1.0, 0.0, 0.7), (1.0, 1.0, 0.0), (-1.0, 0.5, 0.5)):
+        st, tok = oracle_mod.sample(raw, dtype, 500, 50, T, p, u)
+        assert st == 0 and tok.tolist() == top[:, 0].tolist()
+
+
+def test_sample_equal_candidates_inverse_cdf(oracle_mod):
+    # k equal top values: uniform weights, token = the (floor(u k) + 1)-th
+    # lowest index among them
+    cols = [3, 9, 10, 17, 40]
+    x = np.full((1, 64), -5.0, dtype=np.float32)
+    x[0, cols] = 2.0
+    for u in (0.0, 0.19, 0.2, 0.5, 0.79, 0.8, 0.99):
+        st, tok = oracle_mod.sample(x, "f32", 64, 5, 1.0, 1.0, u)
+        assert st == 0 and tok[0] == cols[int(u * 5)]
+    # u exactly on a step (W_j = j, u k = j in binary): the draw is the next one
+    x[0, cols[4]] = -5.0
+    for u in (0.25, 0.5, 0.75):
+        st, tok = oracle_mod.sample(x, "f32", 64, 4, 1.0, 1.0, u)
+        assert st == 0 and tok[0] == cols[int(u * 4)]
+    # top_p exactly on a step (W_2 = 2 = 0.5 W_4): the nucleus keeps two, so
+    # u = 0.9 draws at t = 1.8, the second
+    st, tok = oracle_mod.sample(x, "f32", 64, 4, 1.0, 0.5, 0.9)
+    assert st == 0 and tok[0] == cols[1]
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 3.0])
+def test_sample_two_candidates_analytic(oracle_mod, T):
+    # p(first) = 1 / (1 + exp((b - a) / T)); the fill is exp(-1000 / T) = 0
+    a, b = 1.25, 0.5
+    p1 = 1.0 / (1.0 + math.exp((b - a) / T))
+    x = _row("f32", [b, a])  # the larger value at column 1
+    for u, want in ((p1 - 1e-6, 1), (p1 + 1e-6, 0)):
+        st, tok = oracle_mod.sample(x, "f32", 64, 8, T, 1.0, u)
+        assert st == 0 and tok[0] == want
+
+
+def test_sample_nucleus_closed_form(oracle_mod):
+    # weights 1, 1/2, 1/4 (logits 0, -ln 2, -ln 4 at T = 1): W = 1, 1.5, 1.75;
+    # top_p 0.8 keeps two (1.5 >= 1.4), so u = 0.9 -> t = 1.35 -> second,
+    # u = 0.6 -> t = 0.9 -> first; top_p 0.5 keeps one; top_p 1 keeps all
+    # three: u = 0.9 -> t = 1.575 -> third, 0.6 -> 1.05 -> second,
+    # 0.5 -> 0.875 -> first
+    x = _row("f32", [0.0, -math.log(2.0), -math.log(4.0)])
+    cases = ((0.8, 0.9, 1), (0.8, 0.6, 0), (0.5, 0.99, 0), (1.0, 0.9, 2), (1.0, 0.6, 1), (1.0, 0.5, 0))
+    for p, u, want in cases:
+        st, tok = oracle_mod.sample(x, "f32", 64, 3, 1.0, p, u)
+        assert st == 0 and tok[0] == want, (p, u)
+
+
+def test_sample_frequencies_follow_softmax(oracle_mod):
+    # u on a uniform grid: each candidate is drawn in proportion to its
+    # nucleus-normalised softmax weight (to within one grid step)
+    vals = [1.0, 0.7, 0.2, -0.3, -1.1, -2.0]
+    x = _row("f32", vals)
+    T, p, N = 0.8, 0.9, 2000
+    w = np.exp((np.array(vals) - vals[0]) / T)
+    W = np.cumsum(w)
+    m = int(np.argmax(W >= p * W[-1])) + 1
+    want = w[:m] / W[m - 1] * N
+    grid = (np.arange(N) + 0.5) / N
+    xs = np.repeat(x, N, axis=0)
+    st, tok = oracle_mod.sample(xs, "f32", 64, 6, T, p, grid)
+    assert st == 0
+    counts = np.bincount(tok, minlength=64)[: len(vals)]
+    assert np.all(np.abs(counts[:m] - want) <= 1.0) and counts[m:].sum() == 0
+
+
+def test_sample_infinite_tops(oracle_mod):
+    # two +inf share the mass (lower index first); -inf candidates get none
+    x = np.full((1, 64), -np.inf, dtype=np.float32)
+    x[0, 20] = np.inf
+    x[0, 7] = np.inf
+    x[0, 30] = 5.0
+    for u, want in ((0.1, 7), (0.49, 7), (0.51, 20), (0.99, 20)):
+        st, tok = oracle_mod.sample(x, "f32", 64, 10, 1.0, 1.0, u)
+        assert st == 0 and tok[0] == want
+
+
 # ---------------------------------------------------------------- planted mistakes
 _MUTANTS = {
     "tie_to_higher_index": ("if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
@@ -273,6 +365,9 @@ _MUTANTS = {
     "value_order_by_index": ("if (sorted_index == 1) qsort", "if (sorted_index) qsort"),
     "lengths_read_tail": ("it[c].v = c < len ? widen(row, dtype, c) : -INFINITY;", "it[c].v = widen(row, dtype, c);"),
     "lengths_off_by_one": ("it[c].v = c < len ? widen", "it[c].v = c <= len ? widen"),
+    "sample_ignores_temperature": ("exp((x - x1) / T)", "exp(x - x1)"),
+    "sample_nucleus_strict": ("if (W[j] >= p * W[k - 1]) {", "if (W[j] > p * W[k - 1]) {"),
+    "sample_draw_not_strict": ("if (W[j] > t) {", "if (W[j] >= t) {"),
 }
 
 
@@ -298,6 +393,12 @@ def _pins_pass(oracle_mod):
         test_value_order_is_rank_order(oracle_mod, "bf16")
         test_lengths_match_brute_force_on_neg_inf_tails(oracle_mod, "f32")
         test_lengths_never_read_the_tail(oracle_mod, "bf16")
+        test_sample_greedy_cases(oracle_mod, "f32")
+        test_sample_equal_candidates_inverse_cdf(oracle_mod)
+        test_sample_two_candidates_analytic(oracle_mod, 0.5)
+        test_sample_nucleus_closed_form(oracle_mod)
+        test_sample_frequencies_follow_softmax(oracle_mod)
+        test_sample_infinite_tops(oracle_mod)
     except AssertionError:
         return False
     return True
@@ -313,5 +414,7 @@ def test_planted_mistake_is_caught(oracle_mod, name, monkeypatch):
     lib.oracle_topk.argtypes = oracle_mod._load().oracle_topk.argtypes
     lib.oracle_topk_lengths.restype = ctypes.c_int
     lib.oracle_topk_lengths.argtypes = oracle_mod._load().oracle_topk_lengths.argtypes
+    lib.oracle_sample.restype = ctypes.c_int
+    lib.oracle_sample.argtypes = oracle_mod._load().oracle_sample.argtypes
     monkeypatch.setattr(oracle_mod, "_lib", lib)
     assert not _pins_pass(oracle_mod), "pins did not catch mutant %s" % name
