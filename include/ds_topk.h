@@ -185,6 +185,33 @@ int ds_topk_ex(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_
                int sorted_index, int return_value, void* out_idx, void* out_val, const ds_topk_options* opt,
                void* stream);
 
+/*
+ * ds_topk_sample: one token per row drawn from the row's top-k -- the step
+ * after the selection on the sampler path.  The pages list temperature and
+ * top-p among the generation parameters (CSDN page, section 二 接入层;
+ * zh-TW page, the deepseek-recipe section) without a formula; this is the
+ * textbook one.  With c_1 .. c_k the row's top-k in value order (as
+ * DS_ORDER_VALUE) and x_j their values:
+ *   w_j = exp((x_j - x_1) / T), taken as 1 where x_j == x_1 and as 0 for
+ *         x_j = -inf below a larger x_1;
+ *   W_j = w_1 + ... + w_j;
+ *   m   = the smallest j with W_j >= top_p * W_k (the nucleus; k if none);
+ *   the token is c_j for the smallest j <= m with W_j > u * W_m.
+ * T <= 0 (or NaN) draws greedily: c_1.  u is clamped to [0, 1).
+ *
+ *   temperature, top_p, uniform  device pointers, batch floats each (u: the
+ *                caller's uniform random numbers, one per row).
+ *   out_token    device pointer, batch int32 column indices.
+ * Other arguments, errors (NaN included) and synchronisation as ds_topk.
+ * The weights and sums are fp32: a draw within a few fp32 ulps of a
+ * boundary may land on the neighbouring candidate of the exact (real
+ * number) draw.  The library keeps the k candidates of each row in a
+ * per-(device, stream) buffer of its own.
+ */
+int ds_topk_sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                   const float* temperature, const float* top_p, const float* uniform, int32_t* out_token,
+                   void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* ds_topk_status_string(int status);
 

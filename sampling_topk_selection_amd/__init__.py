@@ -40,7 +40,8 @@ DS_ORDER_VALUE = 2
 
 MAX_K = 4096
 
-EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_ex", "ds_topk_status_string", "ds_topk_last_error",
+EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_ex", "ds_topk_sample", "ds_topk_status_string",
+           "ds_topk_last_error",
            "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_version")
 
 
@@ -81,6 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk_async.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp, vp]
     lib.ds_topk_lengths.restype = ci
     lib.ds_topk_lengths.argtypes = [vp, ci, i64, i64, i64, i32, vp, ci, ci, vp, vp, vp]
+    lib.ds_topk_sample.restype = ci
+    lib.ds_topk_sample.argtypes = [vp, ci, i64, i64, i64, i32, vp, vp, vp, vp, vp]
     lib.ds_topk_ex.restype = ci
     lib.ds_topk_ex.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, ctypes.POINTER(ds_topk_options), vp]
     lib.ds_topk_status_string.restype = ctypes.c_char_p
@@ -119,6 +122,12 @@ def ds_topk_ex(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: 
     opt = ds_topk_options(index_bytes, lengths_ptr, status_dev_ptr)
     return load_library().ds_topk_ex(in_ptr, dtype, batch, n, row_stride, k, sorted_index, return_value,
                                      out_idx_ptr, out_val_ptr, ctypes.byref(opt), stream)
+
+
+def ds_topk_sample(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, temperature_ptr: int,
+                   top_p_ptr: int, uniform_ptr: int, out_token_ptr: int, stream: Optional[int]) -> int:
+    return load_library().ds_topk_sample(in_ptr, dtype, batch, n, row_stride, k, temperature_ptr, top_p_ptr,
+                                         uniform_ptr, out_token_ptr, stream)
 
 
 def ds_topk_async(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, sorted_index: int,
@@ -268,3 +277,26 @@ def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: b
                            status.data_ptr(), stream)
     _check(st)
     return val, idx
+
+
+def sample(x: torch.Tensor, k: int, temperature, top_p, uniform, *, n: Optional[int] = None) -> torch.Tensor:
+    """One token per row of ``x`` drawn from its top-k (see ds_topk_sample in
+    include/ds_topk.h): temperature softmax over the k candidates, top-p
+    nucleus, inverse CDF at ``uniform``.  ``temperature``, ``top_p`` and
+    ``uniform`` are floats or float32 device tensors with one entry per row.
+    Returns int32 [batch] column indices.  Blocks until done."""
+    x, dt, batch, n, row_stride = _marshal(x, k, n)
+
+    def per_row(a, name):
+        if isinstance(a, torch.Tensor):
+            if a.dtype != torch.float32 or not a.is_cuda or a.numel() != batch or not a.is_contiguous():
+                raise ValueError("%s must be a contiguous float32 device tensor with one entry per row" % name)
+            return a
+        return torch.full((batch,), float(a), dtype=torch.float32, device=x.device)
+
+    t, p, u = per_row(temperature, "temperature"), per_row(top_p, "top_p"), per_row(uniform, "uniform")
+    out = torch.empty(batch, dtype=torch.int32, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(ds_topk_sample(x.data_ptr(), dt, batch, n, row_stride, k, t.data_ptr(), p.data_ptr(), u.data_ptr(),
+                          out.data_ptr(), stream))
+    return out

@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ds_topk.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(ROOT, "include", "ds_topk.h")]
+DEPS = [SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
+        os.path.join(ROOT, "include", "ds_topk.h")]
 LIB = os.path.join(HERE, "libds_topk.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
 CALIB_LIB = os.path.join(HERE, "libds_calib.so")

@@ -13,6 +13,7 @@
 #include <utility>
 
 #include "ds_topk.h"
+#include "sample_kernels.hpp"
 #include "topk_kernels.hpp"
 
 namespace {
@@ -299,6 +300,83 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
     return DS_OK;
 }
 
+// ------------------------------------------------------------------ sampling
+// Per-(device, stream) buffers of the value-ordered top-k that sampling reads.
+struct SampleWs {
+    std::mutex mu;
+    void* buf = nullptr;  // idx [rows][k] int32, then values [rows][k]
+    int64_t bytes = 0;
+    int32_t* status = nullptr;
+    int32_t* host_word = nullptr;  // pinned
+};
+std::mutex g_sws_mu;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<SampleWs>> g_sws;
+
+int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+           const float* temperature, const float* top_p, const float* uniform, int32_t* out_token,
+           hipStream_t stream) {
+    g_err.clear();
+    int st = validate(dtype, batch, n, row_stride, k);
+    if (st) return st;
+    if (!in || !temperature || !top_p || !uniform || !out_token)
+        return fail(DS_ERR_INVALID_ARGUMENT, "a pointer argument is NULL");
+    if (((uintptr_t)in) % 16 != 0) return fail(DS_ERR_MISALIGNED, "in is not 16-byte aligned");
+    if (batch == 0) return DS_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    SampleWs* sw;
+    {
+        std::lock_guard<std::mutex> g(g_sws_mu);
+        auto& slot = g_sws[std::make_pair(dev, stream)];
+        if (!slot) slot.reset(new SampleWs());
+        sw = slot.get();
+    }
+    std::lock_guard<std::mutex> g(sw->mu);
+    const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
+    const int64_t idx_bytes = ((batch * k * 4 + 255) / 256) * 256;
+    const int64_t need = idx_bytes + batch * k * es;
+    if (!sw->status) {
+        e = hipMalloc((void**)&sw->status, 256);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(sample status)");
+        e = hipHostMalloc((void**)&sw->host_word, sizeof(int32_t), hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    }
+    if (need > sw->bytes) {
+        if (sw->buf) {
+            e = hipDeviceSynchronize();  // earlier calls on this stream may still read it
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            e = hipFree(sw->buf);
+            sw->buf = nullptr;
+            sw->bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        e = hipMalloc(&sw->buf, (size_t)need);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(sample buffers)");
+        sw->bytes = need;
+    }
+    int32_t* cidx = (int32_t*)sw->buf;
+    void* cval = (uint8_t*)sw->buf + idx_bytes;
+    e = hipMemsetAsync(sw->status, 0, sizeof(int32_t), stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    st = run(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, sw->status, stream);
+    if (st) return st;
+    if (dtype == DS_DTYPE_BF16)
+        hipLaunchKernelGGL(dssample::sample_rows<uint16_t>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
+                           (const uint16_t*)cval, cidx, k, temperature, top_p, uniform, out_token);
+    else
+        hipLaunchKernelGGL(dssample::sample_rows<float>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
+                           (const float*)cval, cidx, k, temperature, top_p, uniform, out_token);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "sample launch");
+    e = hipMemcpyAsync(sw->host_word, sw->status, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (*sw->host_word == DS_ERR_NAN) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
+    return DS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,6 +408,11 @@ int ds_topk_ex(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_
     const int ib = o.index_bytes == 0 ? 4 : o.index_bytes;
     return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, o.status_dev,
                (hipStream_t)stream, o.lengths, ib);
+}
+int ds_topk_sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                   const float* temperature, const float* top_p, const float* uniform, int32_t* out_token,
+                   void* stream) {
+    return sample(in, dtype, batch, n, row_stride, k, temperature, top_p, uniform, out_token, (hipStream_t)stream);
 }
 
 const char* ds_topk_status_string(int status) {

@@ -89,6 +89,10 @@ def test_pointer_errors(pkg):
     assert pkg.ds_topk_async(FAKE, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None, None) == 1  # no status word
     assert pkg.ds_topk_lengths(FAKE, BF, 4, 64, 64, 8, None, 0, 0, FAKE, None, None) == 1  # no lengths
     assert pkg.ds_topk_lengths(FAKE, BF, 4, 64, 64, 8, FAKE, 3, 0, FAKE, None, None) == 1
+    assert pkg.ds_topk_sample(FAKE, BF, 4, 64, 64, 8, None, FAKE, FAKE, FAKE, None) == 1
+    assert pkg.ds_topk_sample(FAKE, BF, 4, 64, 64, 8, FAKE, FAKE, FAKE, None, None) == 1
+    assert pkg.ds_topk_sample(FAKE, BF, 4, 64, 64, 65, FAKE, FAKE, FAKE, FAKE, None) == 1  # k > n
+    assert pkg.ds_topk_sample(FAKE, BF, 4, 8192, 8192, 4097, FAKE, FAKE, FAKE, FAKE, None) == 2  # k > 4096
     for ib in (2, 16):  # index_bytes neither 4 nor 8
         assert pkg.ds_topk_ex(FAKE, BF, 4, 64, 64, 8, 0, 0, FAKE, None, ib) == 1
     for order in (-1, 3):  # not a ds_topk_order
