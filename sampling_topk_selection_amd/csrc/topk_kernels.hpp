@@ -766,7 +766,8 @@ struct ColRanks {
 // (0, kOrderIndex or kOrderValue).  Index order comes from a bitmap of the
 // selected columns and a prefix popcount over it (when the row's bitmap
 // fits in the free LDS), else from a bitonic sort; value order from a
-// bitonic sort of the composites.
+// bitonic sort of the composites, in registers and lane shuffles when k
+// fits one entry per thread, else in LDS.
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, void* out_idx_p,
                      void* out_val) {
@@ -802,16 +803,55 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
         }
         return;
     }
+    if (sorted == kOrderValue && k <= (u32)WG) {
+        // value order, one entry per thread: a bitonic sort, ascending, of
+        // the complemented composites (largest composite first; padding ~0
+        // last) held in registers; partners within a wave exchange by lane
+        // shuffles, partners further apart through LDS
+        u32 P = 1;
+        while (P < k) P <<= 1;
+        u64 key = tid < k ? ~sm.buf[tid] : ~0ull;
+        __syncthreads();  // every entry is read before the LDS exchanges below
+        for (u32 size = 2; size <= P; size <<= 1) {
+            for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
+                u64 other;
+                if (stride < (u32)kWave) {
+                    const u32 lo = __shfl_xor((u32)key, (int)stride, kWave);
+                    const u32 hi = __shfl_xor((u32)(key >> 32), (int)stride, kWave);
+                    other = ((u64)hi << 32) | lo;
+                } else {
+                    sm.buf[tid] = key;
+                    __syncthreads();
+                    other = sm.buf[tid ^ stride];
+                    __syncthreads();
+                }
+                const bool up = (tid & size) == 0, low = (tid & stride) == 0;
+                const u64 mn = key < other ? key : other, mx = key < other ? other : key;
+                key = (up == low) ? mn : mx;
+            }
+        }
+        if (tid < k) {
+            out_idx.put(tid, comp_col<E>(~key));
+            if (retval) ov[tid] = (VT)E::bits(comp_key<E>(~key));
+        }
+        return;
+    }
     // Bitonic sort, ascending, of (column, key) for index order, or of the
     // complemented composites for value order (largest composite first);
     // padding ~0 sorts last either way.
     u32 P = 1;
     while (P < k) P <<= 1;
+    DSTK_PHASE(38);
     for (u32 i = tid; i < P; i += WG) {
         const u64 e = i < k ? sm.buf[i] : 0ull;
         sm.buf[i] = i >= k ? ~0ull : sorted == kOrderValue ? ~e : (((u64)comp_col<E>(e) << 32) | comp_key<E>(e));
     }
     __syncthreads();
+    // Pair t of a stage is (i, i + stride) with i = 2t - (t mod stride); for
+    // strides up to 64 the pairs of one wave's 64 t's lie in one block of
+    // 128 entries, the same block at every such stage, and a wave's LDS
+    // accesses take effect in order: only stages with a longer stride, and
+    // their neighbours, need the workgroup barrier.
     for (u32 size = 2; size <= P; size <<= 1) {
         for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
             for (u32 t = tid; t < P / 2; t += WG) {
@@ -824,9 +864,12 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
                     sm.buf[j] = x;
                 }
             }
-            __syncthreads();
+            const u32 next = stride > 1 ? stride >> 1 : size;  // the next stage's stride
+            if (stride > kWave || next > kWave) __syncthreads();
         }
     }
+    __syncthreads();
+    DSTK_PHASE(39);
     for (u32 i = tid; i < k; i += WG) {
         const u64 s = sm.buf[i];
         if (sorted == kOrderValue) {
