@@ -261,6 +261,17 @@ def main() -> int:
         modes["C4_neg_inf_tails_us"] = round(mode_us(x4, w4, return_value=True), 3)
         modes["C4_lengths_us"] = round(mode_us(x4, w4, return_value=True, lengths=l4), 3)
         modes["C4_valid_bytes"] = int(sum(w4.meta["lengths"]) * 2 + w4.batch * w4.k * 6)
+        # one token per row from the top-k (synchronous calls, with their status readback)
+        g = torch.Generator(device="cpu").manual_seed(3)
+        tt = (0.5 + 1.5 * torch.rand(w3.batch, generator=g)).to(dev)
+        pp = (0.5 + 0.5 * torch.rand(w3.batch, generator=g)).to(dev)
+        uu = torch.rand(w3.batch, generator=g).to(dev)
+        for _ in range(3):
+            pkg.sample(x3, w3.k, tt, pp, uu)
+        t = time.perf_counter()
+        for _ in range(30):
+            pkg.sample(x3, w3.k, tt, pp, uu)
+        modes["C3_sample_sync_call_us"] = round((time.perf_counter() - t) / 30 * 1e6, 1)
 
     if args.calib_copy:
         # a plain copy of the sampler input: known traffic for counter scaling
