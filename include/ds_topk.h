@@ -224,7 +224,9 @@ const char* ds_topk_last_error(void);
  * the pointer checks are skipped).
  */
 typedef struct ds_topk_plan {
-    int32_t segments;        /* workgroups per row; > 1 means split rows + merge */
+    int32_t segments;        /* workgroups per row; > 1 means split rows + merge;
+                                0: rows of at most 2048 columns, one 64-lane
+                                wave each, threads / 64 rows per workgroup */
     int32_t threads;         /* threads per workgroup */
     int32_t tiles_per_chunk; /* tiles whose loads are in flight together; a tile is
                                 one 16-byte vector per thread */

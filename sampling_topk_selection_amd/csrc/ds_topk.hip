@@ -125,6 +125,14 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     return DS_OK;
 }
 
+// Rows this short take one wave each (dstk::topk_small_rows), unless a test
+// forces a segment count; value order there holds up to kSmallValueMax.
+constexpr int64_t kSmallRows = dstk::kSmallWG / dstk::kWave;  // rows per workgroup
+bool use_small(int64_t n, int32_t k, int sorted_index) {
+    return n <= dstk::kSmallN && g_force_segs.load() == 0 &&
+           !(sorted_index == DS_ORDER_VALUE && k > dstk::kSmallValueMax);
+}
+
 // ------------------------------------------------------------------ workspace
 struct Workspace {
     std::mutex mu;
@@ -241,6 +249,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
     if (batch == 0) return DS_OK;
     Plan pl;
     make_plan(dtype, batch, n, k, &pl);
+    const bool small = use_small(n, k, sorted_index);
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -287,7 +296,18 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.flag_value = flag_value;
         prm.flags = (g_flags.load() & dstk::kFlagBitonic) | (index_bytes == 8 ? dstk::kFlagIdx64 : 0);
         prm.lengths = lengths ? lengths + r0 : nullptr;
-        e = launch(pl, prm, rows, stream);
+        if (small) {
+            const int64_t grid = (rows + kSmallRows - 1) / kSmallRows;
+            if (dtype == DS_DTYPE_BF16)
+                hipLaunchKernelGGL(dstk::topk_small_rows<2>, dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0, stream,
+                                   prm, rows);
+            else
+                hipLaunchKernelGGL(dstk::topk_small_rows<4>, dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0, stream,
+                                   prm, rows);
+            e = hipGetLastError();
+        } else {
+            e = launch(pl, prm, rows, stream);
+        }
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
     }
     if (status_dev) return DS_OK;
@@ -440,6 +460,13 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
     if (!plan) return fail(DS_ERR_INVALID_ARGUMENT, "plan is NULL");
     Plan pl;
     make_plan(dtype, batch, n, k, &pl);
+    if (use_small(n, k, sorted_index)) {
+        std::memset(plan, 0, sizeof *plan);
+        plan->threads = dstk::kSmallWG;
+        plan->grid = (batch + kSmallRows - 1) / kSmallRows;
+        plan->workspace_bytes = 256;
+        return DS_OK;
+    }
     plan->segments = pl.segs;
     plan->threads = pl.wg;
     plan->tiles_per_chunk = pl.vpt;

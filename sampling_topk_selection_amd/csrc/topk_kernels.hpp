@@ -2186,3 +2186,163 @@ void topk_rows(Params p) {
 }
 
 }  // namespace dstk
+
+namespace dstk {
+
+// ------------------------------------------------------------------ short rows
+// Rows of at most kSmallN columns: one wave per row, kSmallWG / 64 rows per
+// workgroup (the one-workgroup-per-row kernel would leave most of a 512-lane
+// workgroup idle).  Lane l keeps the composites of columns l, l + 64, ... in
+// registers; a radix select over 11-bit digits, in the wave's own LDS
+// histogram, narrows the k-th composite from the top bits down until its
+// digit's whole sub-bin is kept, which gives T with exactly k composites at
+// or above it.  Kept entries are written in column order by ballot (that is
+// index order too), or gathered and sorted by value.  Only the wave's own
+// LDS is touched, so no workgroup barrier is needed.
+constexpr int kSmallN = 2048;
+constexpr int kSmallWG = 256;
+constexpr int kSmallJ = kSmallN / kWave;         // columns per lane
+constexpr int kSmallValueMax = kBins / 2;        // value order: k the LDS list holds (u64 in the histogram)
+
+template <int EB>
+__global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t rows) {
+    using E = Elem<EB>;
+    using VT = typename std::conditional<EB == 2, uint16_t, uint32_t>::type;
+    constexpr u32 kWaves = kSmallWG / kWave;
+    __shared__ u32 hist_all[kWaves][kBins];
+    const u32 wave = threadIdx.x / kWave, l = lane_id();
+    const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+    if (row >= rows) return;  // the whole wave
+    u32* const hist = hist_all[wave];
+    const u32 kout = (u32)p.k;
+    u32 n = (u32)p.n;
+    if (p.lengths) {
+        const int32_t len = p.lengths[row];
+        n = len < 0 ? 0u : (u32)len < n ? (u32)len : n;
+    }
+    const u32 k = kout < n ? kout : n;
+    const IdxOut out = IdxOut{p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
+    VT* const ov = p.retval ? (VT*)((uint8_t*)p.out_val + (u64)row * kout * EB) : nullptr;
+    for (u32 j = k + l; j < kout; j += kWave) {  // -inf columns past a short row (see write_tail)
+        out.put(j, j);
+        if (ov) ov[j] = EB == 2 ? (VT)0xFF80u : (VT)0xFF800000u;
+    }
+    if (k == 0) return;
+
+    const uint8_t* rin = p.in + row * p.row_stride_bytes;
+    const u32 jn = (n + kWave - 1) / kWave;
+    u64 comp[kSmallJ];
+    bool nan = false;
+#pragma unroll
+    for (u32 j = 0; j < (u32)kSmallJ; ++j) {
+        const u32 col = j * kWave + l;
+        u64 c = 0;
+        if (j < jn && col < n) {
+            const u32 b = EB == 2 ? (u32)((const uint16_t*)rin)[col] : ((const u32*)rin)[col];
+            nan |= E::is_nan(b);
+            c = compose<E>(E::key(b), col);  // never 0
+        }
+        comp[j] = c;
+    }
+    if (__ballot(nan) && l == 0) *p.flag = p.flag_value;
+
+    // radix select: window [sh, fixed) of the composites whose bits at or
+    // above `fixed` equal P's; r = rank of the k-th among them
+    u64 P = 0;
+    int fixed = 64;
+    u32 r = k;
+    for (int level = 0; level < 64 / kHistBits + 1; ++level) {
+        const int sh = fixed > kHistBits ? fixed - kHistBits : 0;
+        const u64 pm = ~low_mask(fixed), wm = low_mask(fixed - sh);
+        for (u32 i = l; i < (u32)kBins; i += kWave) hist[i] = 0;
+#pragma unroll
+        for (u32 j = 0; j < (u32)kSmallJ; ++j)
+            if (j < jn && comp[j] != 0 && (comp[j] & pm) == P) atomicAdd(&hist[(u32)((comp[j] >> sh) & wm)], 1u);
+        // lane l owns digits 2047 - 32 l - i, i < 32 (descending with the lane)
+        u32 s = 0;
+#pragma unroll
+        for (u32 i = 0; i < 32u; ++i) s += hist[kBins - 1u - 32u * l - i];
+        const u32 incl = wave_incl_scan(s);
+        const u64 hm = __ballot(incl >= r);  // not empty: r <= the entries counted
+        const u32 hl = hm ? (u32)__builtin_ctzll(hm) : (u32)kWave - 1u;
+        const u32 above = __builtin_amdgcn_readlane(incl - s, hl);
+        const u32 ci = l < 32u ? hist[kBins - 1u - 32u * hl - l] : 0u;
+        const u32 in2 = wave_incl_scan(ci);
+        const u64 jm = __ballot(above + in2 >= r);
+        const u32 jl = jm ? (u32)__builtin_ctzll(jm) : 31u;
+        const u32 cc = __builtin_amdgcn_readlane(ci, jl);
+        const u32 rr = r - (above + __builtin_amdgcn_readlane(in2, jl) - cc);
+        P |= (u64)(kBins - 1u - 32u * hl - jl) << sh;
+        if (rr >= cc || sh == 0) break;  // the whole sub-bin is kept: exactly k at or above P
+        r = rr;
+        fixed = sh;
+    }
+    const u64 T = P;
+
+    if (p.sorted != kOrderValue) {  // column order: index order, and any order
+        u32 run = 0;
+#pragma unroll
+        for (u32 j = 0; j < (u32)kSmallJ; ++j) {
+            const bool keep = j < jn && comp[j] >= T && comp[j] != 0;
+            const u64 m = __ballot(keep);
+            const u32 pos = run + mbcnt(m);
+            if (keep && pos < k) {
+                out.put(pos, comp_col<E>(comp[j]));
+                if (ov) ov[pos] = (VT)E::bits(comp_key<E>(comp[j]));
+            }
+            run += (u32)__popcll(m);
+        }
+        return;
+    }
+    // value order: gather the kept composites (complemented: ascending sort
+    // puts the largest first, padding ~0 last) into the wave's LDS, then a
+    // bitonic sort there, or in registers when one lane each suffices
+    u64* const list = (u64*)hist;
+    u32 run = 0;
+#pragma unroll
+    for (u32 j = 0; j < (u32)kSmallJ; ++j) {
+        const bool keep = j < jn && comp[j] >= T && comp[j] != 0;
+        const u64 m = __ballot(keep);
+        const u32 pos = run + mbcnt(m);
+        if (keep && pos < (u32)kSmallValueMax) list[pos] = ~comp[j];
+        run += (u32)__popcll(m);
+    }
+    u32 Pn = 1;
+    while (Pn < k) Pn <<= 1;
+    for (u32 i = k + l; i < Pn; i += kWave) list[i] = ~0ull;
+    if (Pn <= (u32)kWave) {
+        u64 key = l < Pn ? list[l] : ~0ull;
+        for (u32 size = 2; size <= Pn; size <<= 1)
+            for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
+                const u32 lo = __shfl_xor((u32)key, (int)stride, kWave);
+                const u32 hi = __shfl_xor((u32)(key >> 32), (int)stride, kWave);
+                const u64 other = ((u64)hi << 32) | lo;
+                const bool up = (l & size) == 0, low = (l & stride) == 0;
+                const u64 mn = key < other ? key : other, mx = key < other ? other : key;
+                key = (up == low) ? mn : mx;
+            }
+        if (l < k) {
+            out.put(l, comp_col<E>(~key));
+            if (ov) ov[l] = (VT)E::bits(comp_key<E>(~key));
+        }
+        return;
+    }
+    for (u32 size = 2; size <= Pn; size <<= 1)
+        for (u32 stride = size >> 1; stride > 0; stride >>= 1)
+            for (u32 t = l; t < Pn / 2; t += kWave) {
+                const u32 i = 2 * t - (t & (stride - 1)), j = i + stride;
+                const bool up = (i & size) == 0;
+                const u64 x = list[i], y = list[j];
+                if ((x > y) == up) {
+                    list[i] = y;
+                    list[j] = x;
+                }
+            }
+    for (u32 i = l; i < k; i += kWave) {
+        const u64 c = ~list[i];
+        out.put(i, comp_col<E>(c));
+        if (ov) ov[i] = (VT)E::bits(comp_key<E>(c));
+    }
+}
+
+}  // namespace dstk
