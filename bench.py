@@ -261,6 +261,14 @@ def main() -> int:
         modes["C4_neg_inf_tails_us"] = round(mode_us(x4, w4, return_value=True), 3)
         modes["C4_lengths_us"] = round(mode_us(x4, w4, return_value=True, lengths=l4), 3)
         modes["C4_valid_bytes"] = int(sum(w4.meta["lengths"]) * 2 + w4.batch * w4.k * 6)
+        # many short rows: one wave per row
+        for (bsz, nn, kk) in ((4096, 256, 64), (16384, 128, 16)):
+            gs = torch.Generator(device="cpu").manual_seed(bsz + nn)
+            xs = torch.randn(bsz, nn, generator=gs).to(torch.bfloat16).to(dev)
+
+            class _W:  # the shape mode_us needs
+                k, n = kk, nn
+            modes["short_rows_bf16_%dx%d_k%d_us" % (bsz, nn, kk)] = round(mode_us(xs, _W, return_value=True), 3)
         # one token per row from the top-k (synchronous calls, with their status readback)
         g = torch.Generator(device="cpu").manual_seed(3)
         tt = (0.5 + 1.5 * torch.rand(w3.batch, generator=g)).to(dev)
