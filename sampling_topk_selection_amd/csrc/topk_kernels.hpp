@@ -9,22 +9,30 @@
 // threshold approach the true k-th value early.
 //
 // MI355X design:
-//   * one workgroup streams one row segment with 16-byte loads, the next tile
-//     in flight while the current one is filtered;
+//   * one workgroup streams one row segment with 16-byte buffer loads, in
+//     chunks of tiles, the next chunk in flight while the current one is
+//     filtered;
 //   * every element is mapped to a 64-bit composite key
 //         (order-preserving value key << ...) | (~column << ...)
 //     so that the operator's total order (value, then +0 over -0, then the
 //     lower column) is plain unsigned order and all keys are distinct;
-//   * a float compare against the threshold's value rejects most elements
-//     in one VALU op (it also lets NaN through, to be caught exactly);
-//   * survivors are checked exactly and appended to an LDS buffer with one
-//     ballot and one LDS atomic per wave and tile;
-//   * the buffer is reduced to k by an MSD radix select in LDS; the k-th
-//     composite becomes the new admission bound;
-//   * short batches split each row over several workgroups; each writes its
-//     local top-k to a workspace and the last one to finish (agent-scope
-//     ticket) merges them with the same filter/compaction machinery;
-//   * index-ordered output is a bitonic sort of the k survivors in LDS.
+//   * the first chunk is counted in an 11-bit histogram of composites and
+//     the bin of its k-th entry seeds the admission bound;
+//   * a float compare against the bound's value rejects most elements in one
+//     VALU op (it also lets NaN through, to be caught exactly); survivors go
+//     to the wave's own region of an LDS buffer behind a scalar write
+//     pointer, with no atomics and no barrier;
+//   * a full region, and a few scheduled points, move the regions together
+//     (counting them), reduce the buffer if needed and raise the bound;
+//   * short batches split each row over several workgroups; each publishes
+//     its entries from the bin of its k-th up, by top digit, with a
+//     directory of per-bin counts, and the last one to finish (agent-scope
+//     ticket) merges them: row histogram from the directories, the share of
+//     each segment at or above the row's k-th bin, exact selection;
+//   * the exact k-th composite comes from radix levels inside its bin (or a
+//     one-wave ranking when few entries remain); index-ordered output ranks
+//     columns through a bitmap of the selected columns, value order sorts;
+//   * rows of at most 2048 columns take one wave each (topk_small_rows).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -2029,8 +2037,10 @@ void topk_rows(Params p) {
     DSTK_PHASE(4);
 
     // ---- merge.  Every element of the row's top-k is in some segment's
-    // published list.  Row bound: the largest segment bound, or the smallest
-    // q-bound if that is larger; only digits at or above it are counted.
+    // published list.  One round trip reads every segment's metadata and the
+    // head of its directory; the row histogram, a one-wave walk to the bin of
+    // the row's k-th entry and the segments' shares follow, then the shares
+    // are loaded and the selection finishes as for a single segment.
     const u32 cap = (u32)p.pub_cap;
     const u64* rc = p.ws_cand + (u64)row * S * cap;
     const u32* rdir = p.ws_dir + (u64)row * S * kBins;
