@@ -240,3 +240,36 @@ def test_value_order_edges(pkg, oracle_mod, dtype, levels):
             log("value order %s levels=%d n=%d k=%d" % (dtype, levels, n, k))
             for segs in (0, 1, 4):
                 _check(pkg, oracle_mod, raw, dtype, n, k, 2, segs)
+
+
+@pytest.mark.parametrize("cfg", ["C3", "C2"])
+def test_async_call_in_a_graph(pkg, oracle_mod, cfg):
+    # ds_topk_async captured in a HIP graph (after a warm-up call sized the
+    # workspace) and replayed several times, with eager calls in between:
+    # every replay gives the eager answer.
+    import torch
+
+    from workloads import make_workload
+
+    w = make_workload(cfg, batch=8)
+    x = to_device(w.raw, w.dtype)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    log("graph replay %s" % cfg)
+    ref_v, ref_i = pkg.topk(x, w.k, sorted_index=True, return_value=True, n=w.n)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out_v = torch.empty_like(ref_v)
+        out_i = torch.empty_like(ref_i)
+        pkg.topk_async(x, w.k, status, sorted_index=True, n=w.n, out=(out_v, out_i))  # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pkg.topk_async(x, w.k, status, sorted_index=True, n=w.n, out=(out_v, out_i))
+    for rep in range(4):
+        out_i.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_i, ref_i) and torch.equal(out_v, ref_v), "replay %d" % rep
+        pkg.topk(x, w.k, sorted_index=False, return_value=False, n=w.n)  # eager work between replays
+    assert int(status.item()) == 0
