@@ -773,9 +773,9 @@ struct ColRanks {
 // Writes the k entries of buf[0, k) in the order `sorted` asks for
 // (0, kOrderIndex or kOrderValue).  Index order comes from a bitmap of the
 // selected columns and a prefix popcount over it (when the row's bitmap
-// fits in the free LDS), else from a bitonic sort; value order from a
-// bitonic sort of the composites, in registers and lane shuffles when k
-// fits one entry per thread, else in LDS.
+// fits in the free LDS), else from a bitonic sort; value order from ranks
+// (sorted runs of one wave each and binary searches) when k fits one entry
+// per thread, else from a bitonic sort of the composites in LDS.
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, void* out_idx_p,
                      void* out_val) {
@@ -812,35 +812,46 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
         return;
     }
     if (sorted == kOrderValue && k <= (u32)WG) {
-        // value order, one entry per thread: a bitonic sort, ascending, of
-        // the complemented composites (largest composite first; padding ~0
-        // last) held in registers; partners within a wave exchange by lane
-        // shuffles, partners further apart through LDS
-        u32 P = 1;
-        while (P < k) P <<= 1;
-        u64 key = tid < k ? ~sm.buf[tid] : ~0ull;
-        __syncthreads();  // every entry is read before the LDS exchanges below
-        for (u32 size = 2; size <= P; size <<= 1) {
-            for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
-                u64 other;
-                if (stride < (u32)kWave) {
-                    const u32 lo = __shfl_xor((u32)key, (int)stride, kWave);
-                    const u32 hi = __shfl_xor((u32)(key >> 32), (int)stride, kWave);
-                    other = ((u64)hi << 32) | lo;
-                } else {
-                    sm.buf[tid] = key;
-                    __syncthreads();
-                    other = sm.buf[tid ^ stride];
-                    __syncthreads();
-                }
-                const bool up = (tid & size) == 0, low = (tid & stride) == 0;
-                const u64 mn = key < other ? key : other, mx = key < other ? other : key;
-                key = (up == low) ? mn : mx;
-            }
+        // value order, one entry per thread.  The composites are distinct,
+        // so an entry's output slot is the number of selected composites
+        // above it.  Each wave first ranks its 64 entries among themselves
+        // (lane broadcasts) and stores them in that order, as a descending
+        // run; the count above an entry in every run (its own included) is
+        // then a binary search of that run.  Threads past k hold 0, which
+        // no composite equals and which sorts below all of them.
+        const u32 wave = tid / kWave, l = lane_id();
+        const u64 e = tid < k ? sm.buf[tid] : 0ull;
+        const u32 elo = (u32)e, ehi = (u32)(e >> 32);
+        u32 local = 0;
+#pragma unroll
+        for (int j = 0; j < kWave; ++j) {
+            const u64 o = ((u64)(u32)__builtin_amdgcn_readlane((int)ehi, j) << 32) |
+                          (u32)__builtin_amdgcn_readlane((int)elo, j);
+            local += o > e ? 1u : 0u;
         }
+        DSTK_PHASE(42);
+        if (tid >= k) local = l;  // the zeros keep distinct slots behind the entries
+        __syncthreads();          // every entry is read before the runs overwrite buf
+        DSTK_PHASE(38);
+        sm.buf[wave * kWave + local] = e;
+        __syncthreads();
+        u32 rank = 0;
+#pragma unroll
+        for (u32 w = 0; w < (u32)(WG / kWave); ++w) {
+            const u64* run = sm.buf + w * kWave;
+            u32 c = 0;
+#pragma unroll
+            for (u32 st = kWave / 2; st > 0; st >>= 1) c += run[c + st - 1] > e ? st : 0u;
+            rank += c + (run[c] > e ? 1u : 0u);
+        }
+        DSTK_PHASE(39);
+        __syncthreads();  // the runs are read; reorder through buf for coalesced stores
+        if (tid < k) sm.buf[rank] = e;
+        __syncthreads();
         if (tid < k) {
-            out_idx.put(tid, comp_col<E>(~key));
-            if (retval) ov[tid] = (VT)E::bits(comp_key<E>(~key));
+            const u64 s = sm.buf[tid];
+            out_idx.put(tid, comp_col<E>(s));
+            if (retval) ov[tid] = (VT)E::bits(comp_key<E>(s));
         }
         return;
     }
@@ -1173,8 +1184,10 @@ template <class E, int WG, int CAP>
 __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
                                             int flags, void* out_idx_p, void* out_val) {
     const IdxOut out_idx{out_idx_p, flags & kFlagIdx64};
+    DSTK_PHASE(40);
     __syncthreads();
     keep_at_least<WG, CAP>(sm, 0, cnt, T);
+    DSTK_PHASE(41);
     emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx.p, out_val);
 }
 
