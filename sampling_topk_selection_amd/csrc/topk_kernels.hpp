@@ -236,6 +236,12 @@ struct Smem {
 #ifndef DSTK_PROBE_FLUSH
 #define DSTK_PROBE_FLUSH() ((void)0)
 #endif
+// Ends the wave where the last output of a workgroup is written: the
+// callers have nothing left to do, and returning from the out-of-line
+// function would first reload the registers it saved.
+#ifndef DSTK_EXIT
+#define DSTK_EXIT() __builtin_amdgcn_endpgm()
+#endif
 
 // ------------------------------------------------------------------ wave helpers
 // Cross-lane steps use DPP (row_shr, quad_perm, row mirrors, row_bcast15/31),
@@ -1673,17 +1679,20 @@ struct Slot {
 };
 
 // Exact selection of the k largest of buf[0, cnt) (bin b1 holds the k-th,
-// rank r1 of c1 inside it) and output; then the NaN report.
+// rank r1 of c1 inside it) and output, the −inf tail up to kout, then the
+// NaN report; the workgroup ends here.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 n, int sorted,
-                                             int retval, int flags, void* row_idx_p, void* row_val, int32_t* flag,
-                                             int32_t flag_value) {
+__device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
+                                             int sorted, int retval, int flags, void* row_idx_p, void* row_val,
+                                             int32_t* flag, int32_t flag_value) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
     DSTK_PHASE(5);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
+    if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
     __syncthreads();
     if (threadIdx.x == 0 && sm.nan) *flag = flag_value;
+    DSTK_EXIT();
 }
 
 // Merge when the boundary bin is too large for the buffer (heavy ties
@@ -1970,11 +1979,8 @@ void topk_rows(Params p) {
     if (p.segs == 1) {
         block_locate<WG, CAP>(sm, k, 0u, true);
         DSTK_PHASE(2);
-        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, n, p.sorted, p.retval,
-                                    p.flags, row_idx.p, row_val, p.flag, p.flag_value);
-        if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
-        DSTK_PHASE(6);
-        DSTK_PROBE_FLUSH();
+        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, kout, n, p.sorted,
+                                    p.retval, p.flags, row_idx.p, row_val, p.flag, p.flag_value);
         return;
     }
 
@@ -2200,12 +2206,8 @@ void topk_rows(Params p) {
     }
     __syncthreads();
     DSTK_PHASE(14);
-    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, n, p.sorted, p.retval, p.flags, row_idx.p, row_val,
-                                p.flag,
-                                p.flag_value);
-    if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
-    DSTK_PHASE(6);
-    DSTK_PROBE_FLUSH();
+    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, kout, n, p.sorted, p.retval, p.flags, row_idx.p, row_val,
+                                p.flag, p.flag_value);
 }
 
 }  // namespace dstk
