@@ -236,9 +236,9 @@ struct Smem {
 #ifndef DSTK_PROBE_FLUSH
 #define DSTK_PROBE_FLUSH() ((void)0)
 #endif
-// Ends the wave where the last output of a workgroup is written: the
-// callers have nothing left to do, and returning from the out-of-line
-// function would first reload the registers it saved.
+// Ends the wave where the last output of a workgroup is written (nothing
+// follows it on any path; a return from an out-of-line caller would first
+// reload the registers that caller saved).
 #ifndef DSTK_EXIT
 #define DSTK_EXIT() __builtin_amdgcn_endpgm()
 #endif
@@ -1012,7 +1012,7 @@ __device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool
 // number of larger ones to the entry's rank.  side_count must be zero on
 // entry; sm.seg_count[0, 64) is used for the ranks.
 template <int WG, int CAP>
-__device__ __noinline__ u64 side_select(Smem<CAP>& sm, u32 cnt, u64 mask, u64 prefix, u32 rr) {
+__device__ __forceinline__ u64 side_select(Smem<CAP>& sm, u32 cnt, u64 mask, u64 prefix, u32 rr) {
     static_assert(WG / kWave * 8 >= kWave, "eight entries compared per wave");
     const u32 tid = threadIdx.x, l = lane_id(), wave = tid / kWave;
     u32* const rank = sm.seg_count;
@@ -1294,7 +1294,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
 // follows every wave's last append and wfill store.  (Out of line: it runs
 // a few times per workgroup, and the scan keeps its registers.)
 template <class E, int WG, int CAP>
-__device__ __noinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
+__device__ __forceinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
     constexpr u32 kWaves = WG / kWave;
     const u32 tid = threadIdx.x;
     // Entry j of the concatenation lies at cbase + j plus the unused tails
@@ -1405,7 +1405,7 @@ __device__ __forceinline__ u32 move_regions(Smem<CAP>& sm, const RegionMap<WG>& 
 // sm.nan.  Call after a barrier that follows every wave's last append and
 // wfill store; returns after a barrier.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
+__device__ __forceinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
     const u32 wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const u32 fill = __builtin_amdgcn_readfirstlane(sm.wfill[wave]);
     const u32 rb = cbase + wave * R;
@@ -1440,7 +1440,7 @@ __device__ __noinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
 // sm.L, which make_room may have raised); sm.count holds the new count.
 // Returns after a barrier.
 template <class E, int WG, int CAP>
-__device__ __noinline__ u64 raise_bound(Smem<CAP>& sm, u32 cnt, u32 room, u32 k, u64 L) {
+__device__ __forceinline__ u64 raise_bound(Smem<CAP>& sm, u32 cnt, u32 room, u32 k, u64 L) {
     if (room ? cnt > (u32)CAP - room : (cnt > (u32)CAP / 2 && cnt > k)) {
         make_room<E, WG, CAP>(sm, cnt, k, room);
     } else {
@@ -1682,7 +1682,7 @@ struct Slot {
 // rank r1 of c1 inside it) and output, the −inf tail up to kout, then the
 // NaN report; the workgroup ends here.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
+__device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
                                              int sorted, int retval, int flags, void* row_idx_p, void* row_val,
                                              int32_t* flag, int32_t flag_value) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
