@@ -242,6 +242,20 @@ def test_value_order_edges(pkg, oracle_mod, dtype, levels):
                 _check(pkg, oracle_mod, raw, dtype, n, k, 2, segs)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("levels", [0, 3])
+def test_value_order_rank_sizes(pkg, oracle_mod, dtype, levels):
+    # Value order for k up to the workgroup size ranks each wave's entries as
+    # one run of 64: k just below, at and above a run boundary and at the
+    # largest such k, through one workgroup per row and through the merge.
+    n = 20011
+    raw = make_edge_rows(dtype, 4, n, seed=77 + levels, levels=levels, specials=0.02)
+    for k in (63, 64, 65, 129, 448, 511, 512, 513):
+        log("value order ranks %s levels=%d k=%d" % (dtype, levels, k))
+        for segs in (0, 1, 4):
+            _check(pkg, oracle_mod, raw, dtype, n, k, 2, segs)
+
+
 @pytest.mark.parametrize("cfg", ["C3", "C2"])
 def test_async_call_in_a_graph(pkg, oracle_mod, cfg):
     # ds_topk_async captured in a HIP graph (after a warm-up call sized the
