@@ -1291,8 +1291,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
 // the regions' concatenation goes to cbase + j, at or below where it is,
 // and each batch is read before it is written, so nothing is overwritten
 // before it has been read.  A NaN sets sm.nan.  Call after a barrier that
-// follows every wave's last append and wfill store.  (Out of line: it runs
-// a few times per workgroup, and the scan keeps its registers.)
+// follows every wave's last append and wfill store.
 template <class E, int WG, int CAP>
 __device__ __forceinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
     constexpr u32 kWaves = WG / kWave;
@@ -1575,10 +1574,9 @@ __device__ __forceinline__ bool check_pending(Smem<CAP>& sm, ScanState& st, bool
 // workgroup, raise the bound; with tiles left, reload them (from the cache)
 // and append them, and repeat.  With that much room every region holds one
 // wave's tile, so each round appends at least one tile of every waiting
-// wave, and at most NV + 1 rounds are taken.  Out of line: the common path
-// keeps its registers.
+// wave, and at most NV + 1 rounds are taken.
 template <class E, int WG, int NV, int CAP>
-__device__ __noinline__ ScanState rare_rounds(Smem<CAP>& sm, ScanCtx cx, ScanState st, VecBases<NV> vb, u32 rtile,
+__device__ __forceinline__ ScanState rare_rounds(Smem<CAP>& sm, ScanCtx cx, ScanState st, VecBases<NV> vb, u32 rtile,
                                               bool again) {
     constexpr u32 kTileElems = WG * E::kPerVec;
     for (u32 round = 0;; ++round) {
