@@ -32,8 +32,14 @@ constexpr int64_t kMinSegElems = 8192;  // and at least this many: below it the 
 #ifndef DS_TOPK_TILES_PER_CHUNK_BF16
 #define DS_TOPK_TILES_PER_CHUNK_BF16 2
 #endif
+// bf16 with k > 1024 (the larger buffer): one more tile in flight pays
+// there (measured), while it slows the smaller-k shapes
+#ifndef DS_TOPK_TILES_PER_CHUNK_BF16_BIGK
+#define DS_TOPK_TILES_PER_CHUNK_BF16_BIGK 3
+#endif
 constexpr int kChunkF32 = DS_TOPK_TILES_PER_CHUNK_F32;
 constexpr int kChunkBf16 = DS_TOPK_TILES_PER_CHUNK_BF16;
+constexpr int kChunkBf16BigK = DS_TOPK_TILES_PER_CHUNK_BF16_BIGK;
 constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
 
 thread_local std::string g_err;
@@ -88,9 +94,10 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     pl->eb = dtype == DS_DTYPE_BF16 ? 2 : 4;
     const int epv = 16 / pl->eb;
     pl->wg = 512;
-    pl->vpt = pl->eb == 2 ? kChunkBf16 : kChunkF32;  // 16-byte loads in flight per thread (one chunk)
     pl->depth = 0;
     pl->cap = k <= 1024 ? 8192 : 16384;
+    // 16-byte loads in flight per thread (one chunk)
+    pl->vpt = pl->eb == 4 ? kChunkF32 : pl->cap == 8192 ? kChunkBf16 : kChunkBf16BigK;
     pl->pub_cap = 2 * k + 1024 < pl->cap ? 2 * k + 1024 : pl->cap;
     pl->n_vec = (int)((n + epv - 1) / epv);
     int64_t s;
@@ -221,15 +228,17 @@ hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The instances make_plan can choose (element bytes, capacity).
+// The instances make_plan can choose (element bytes, capacity).  (The
+// fp32 instances come first in the code object: the sampler kernel's
+// timing was measured in that placement.)
 hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s) {
     const int64_t grid = rows * pl.segs;
-    if (pl.eb == 2) {
-        if (pl.cap == 8192) return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
-        return launch_one<2, 512, kChunkBf16, 16384>(prm, grid, s);
+    if (pl.eb == 4) {
+        if (pl.cap == 8192) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
+        return launch_one<4, 512, kChunkF32, 16384>(prm, grid, s);
     }
-    if (pl.cap == 8192) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
-    return launch_one<4, 512, kChunkF32, 16384>(prm, grid, s);
+    if (pl.cap == 8192) return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
+    return launch_one<2, 512, kChunkBf16BigK, 16384>(prm, grid, s);
 }
 
 int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
