@@ -2061,7 +2061,7 @@ void topk_rows(Params p) {
     const u32 cap = (u32)p.pub_cap;
     const u64* rc = p.ws_cand + (u64)row * S * cap;
     const u32* rdir = p.ws_dir + (u64)row * S * kBins;
-    constexpr u32 kDirCache = 32;  // directory entries read with the metadata
+    constexpr u32 kDirCache = 16;  // directory entries read with the metadata
     u64* mc = sm.buf;                                 // [S][4] metadata
     u32* dc = (u32*)(sm.buf + 4 * S);                 // [S][kDirCache] directory heads
     for (u32 i = tid; i < S * 4; i += WG) mc[i] = ld_agent(&p.ws_meta[(u64)row * S * 4 + i]);
