@@ -2318,8 +2318,9 @@ __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t ro
         return;
     }
     // value order: gather the kept composites (complemented: ascending sort
-    // puts the largest first, padding ~0 last) into the wave's LDS, then a
-    // bitonic sort there, or in registers when one lane each suffices
+    // puts the largest first, padding ~0 last) into the wave's LDS, then
+    // ranks by lane broadcasts when one lane each suffices, else a bitonic
+    // sort there
     u64* const list = (u64*)hist;
     u32 run = 0;
 #pragma unroll
@@ -2333,20 +2334,21 @@ __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t ro
     u32 Pn = 1;
     while (Pn < k) Pn <<= 1;
     for (u32 i = k + l; i < Pn; i += kWave) list[i] = ~0ull;
-    if (Pn <= (u32)kWave) {
-        u64 key = l < Pn ? list[l] : ~0ull;
-        for (u32 size = 2; size <= Pn; size <<= 1)
-            for (u32 stride = size >> 1; stride > 0; stride >>= 1) {
-                const u32 lo = __shfl_xor((u32)key, (int)stride, kWave);
-                const u32 hi = __shfl_xor((u32)(key >> 32), (int)stride, kWave);
-                const u64 other = ((u64)hi << 32) | lo;
-                const bool up = (l & size) == 0, low = (l & stride) == 0;
-                const u64 mn = key < other ? key : other, mx = key < other ? other : key;
-                key = (up == low) ? mn : mx;
-            }
+    if (k <= (u32)kWave) {
+        // one entry per lane: the complemented composites are distinct, so
+        // an entry's slot is the number of entries below it, counted over
+        // lane broadcasts
+        const u64 key = l < k ? list[l] : ~0ull;
+        const u32 khi = (u32)(key >> 32), klo = (u32)key;
+        u32 rank = 0;
+        for (u32 j = 0; j < k; ++j) {
+            const u64 o = ((u64)(u32)__builtin_amdgcn_readlane((int)khi, (int)j) << 32) |
+                          (u32)__builtin_amdgcn_readlane((int)klo, (int)j);
+            rank += o < key ? 1u : 0u;
+        }
         if (l < k) {
-            out.put(l, comp_col<E>(~key));
-            if (ov) ov[l] = (VT)E::bits(comp_key<E>(~key));
+            out.put(rank, comp_col<E>(~key));
+            if (ov) ov[rank] = (VT)E::bits(comp_key<E>(~key));
         }
         return;
     }
