@@ -218,7 +218,7 @@ def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: b
     """Top-k of each row of ``x`` ([batch, n], bf16 or fp32, on the device).
 
     Returns ``(values, indices)``; values is None when ``return_value`` is
-    False.  Indices are int32.  ``sorted_index`` writes each row's indices in
+    False.  Indices are ``indices_type``.  ``sorted_index`` writes each row's indices in
     ascending order, ``sorted_value`` largest value first (ties by lower
     index); neither leaves the order free.  ``n`` restricts the selection to
     the first n columns (the rest of each row is padding).  ``lengths`` (an
