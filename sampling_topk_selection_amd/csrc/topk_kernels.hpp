@@ -267,20 +267,19 @@ __device__ __forceinline__ u32 fresh_copy(u32 x) {
     return y;
 }
 
-// Count bin d of each lane with `valid` in hist.  When all of them fall in
-// one bin (runs of equal values: the padding of short rows, quantized
-// scores) one atomic adds them all; 64 atomics on one address would be
-// serialized.
+// Count bin d of each lane with `valid` in hist.  The lanes in the first
+// active lane's bin are added by one atomic (all of them, for runs of equal
+// values: the padding of short rows, quantized scores; often the most
+// crowded bin otherwise), the others one by one: atomics that several lanes
+// aim at one address are serialized.
 __device__ __forceinline__ void hist_add(u32* hist, u32 d, bool valid) {
     const u64 act = __ballot(valid);
     if (act == 0) return;
     const u32 lead = (u32)__builtin_ctzll(act);
     const u32 first = __builtin_amdgcn_readlane(d, lead);
-    if (__ballot(valid && d == first) == act) {
-        if (__lane_id() == lead) atomicAdd(&hist[hidx(first)], (u32)__popcll(act));
-    } else if (valid) {
-        atomicAdd(&hist[hidx(d)], 1u);
-    }
+    const u64 same = __ballot(valid && d == first);
+    if (__lane_id() == lead) atomicAdd(&hist[hidx(first)], (u32)__popcll(same));
+    if (valid && d != first) atomicAdd(&hist[hidx(d)], 1u);
 }
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
