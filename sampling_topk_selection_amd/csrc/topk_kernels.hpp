@@ -1255,7 +1255,7 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
         return;
     }
     const ColRanks<WG> cr(bm, lp, pitch);
-    __syncthreads();  // the histogram may still be read by the last locate
+    if (bm == sm.hist) __syncthreads();  // the histogram may still be read by the last locate
     for (u32 w = tid; w < cr.table_words(); w += WG) bm[w] = 0;
     __syncthreads();
     for (u32 i = tid; i < cnt; i += WG) {
