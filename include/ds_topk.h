@@ -7,8 +7,9 @@
  *
  * The operation (CSDN page "DeepSeek 一次开源三个仓库", section 三 算子层:
  * a top-k operator for sparse-attention indexing and for sampling, small k
- * only, at most 4096; usage `values, indices = deep_select.topk(x, topk,
- * sorted_index=..., indices_type=torch.int32)`):
+ * only, at most 4096; its usage example is a topk(x, k) call with a
+ * sorted-index flag and an index-type option that returns the values and
+ * the indices):
  *
  *   For every row r of a [batch][row_stride] matrix, select the k largest of
  *   the elements in columns [0, n) and return their column indices (int32)
@@ -113,15 +114,25 @@ enum ds_topk_status {
  *   stream       hipStream_t the work is enqueued on.
  *
  * Ownership: the caller owns in, out_idx, out_val and the stream.  The
- * library owns a per-(device, stream) workspace that it allocates on first
- * use, grows when a larger call needs it (growing synchronises the device)
- * and keeps until the process exits.
+ * library owns a per-(device, stream) workspace (split-row lists, their
+ * metadata and digit directories, tickets; a pinned host word for the NaN
+ * status of synchronous calls).  It is allocated on first use and grows when a larger call needs
+ * it: growth allocates a new block, clears it with a memset ordered on
+ * `stream` and keeps the old block until the process exits or
+ * ds_topk_release_stream, so work already queued, or a graph captured
+ * earlier, never sees freed memory.  Growth never synchronises.
  *
- * Synchronisation: the call enqueues the kernel(s) on `stream`, then waits
- * for the stream so that it can return DS_ERR_NAN; when it returns, the
- * outputs are complete.  Argument errors are returned before any HIP call,
- * and nothing is written.  Calls on different streams may run concurrently;
- * they use different workspaces.
+ * Synchronisation: the call enqueues the kernel(s) on `stream`, waits for
+ * the stream, then reads the NaN status from the pinned host word the
+ * kernels store it into; when it returns, the outputs are complete.
+ * Argument errors are returned before any HIP call, and nothing is
+ * written.  Calls on different streams may run concurrently; they use
+ * different workspaces.  Calls on one stream share its workspace, so they
+ * must run in stream order: a graph captured from ds_topk_async on a stream
+ * must be replayed on that stream (or in order with its other calls), never
+ * concurrently with them.  A call whose workspace would have to grow while
+ * `stream` is capturing returns DS_ERR_HIP (make one uncaptured call of the
+ * largest shape on the stream first).
  */
 int ds_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
             int sorted_index, int return_value, int32_t* out_idx, void* out_val, void* stream);
@@ -235,13 +246,15 @@ typedef struct ds_topk_plan {
     int32_t tiles_per_segment;
     int64_t grid;            /* workgroups launched */
     int64_t workspace_bytes; /* device workspace this call needs */
+    int32_t publish_capacity;/* split rows: most entries one segment publishes */
 } ds_topk_plan;
 
 int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
                      int sorted_index, int return_value, ds_topk_plan* plan);
 
 /*
- * Tuning overrides, process-wide (for tests and measurements):
+ * Tuning overrides for tests and measurements.  They apply to the calls the
+ * calling thread makes (thread-local state; other threads keep their own).
  * segments > 0 forces that many workgroups per row (clamped to what the row
  * length allows); 0 restores the automatic choice.  tile_seed changes the
  * pseudo-random tile visiting order (the result never depends on it); 0
@@ -250,6 +263,14 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
  */
 #define DS_TOPK_FORCE_BITONIC 1
 void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed, int32_t flags);
+
+/*
+ * Waits for `stream`, then frees the workspace and sampling buffers the
+ * library holds for (current device, stream), retired blocks included.  For
+ * servers that create and destroy streams.  No graph captured on the stream
+ * may be replayed afterwards.  Returns DS_OK, or DS_ERR_HIP.
+ */
+int ds_topk_release_stream(void* stream);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int ds_topk_version(void);

@@ -5,9 +5,8 @@
  *
  * What it computes is the plain definition of the operator the pages describe
  * (CSDN page "DeepSeek 一次开源三个仓库", section 三 算子层: per row, return the
- * k largest entries, values and indices, k <= 4096; usage example
- * `values, indices = deep_select.topk(x, topk, sorted_index=..., indices_type=
- * torch.int32)`).  The pages' blocked scan / threshold / compaction algorithm
+ * k largest entries, values and indices, k <= 4096; the usage example there
+ * is a topk(x, k) call with a sorted-index flag and an index-type option).  The pages' blocked scan / threshold / compaction algorithm
  * only prunes elements that cannot be among the k largest, so it reaches this
  * same result; the oracle therefore does not follow that algorithm -- it sorts.
  *

@@ -41,8 +41,8 @@ DS_ORDER_VALUE = 2
 MAX_K = 4096
 
 EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_ex", "ds_topk_sample", "ds_topk_status_string",
-           "ds_topk_last_error",
-           "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_version")
+           "ds_topk_last_error", "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_release_stream",
+           "ds_topk_version")
 
 
 class TopkError(RuntimeError):
@@ -55,7 +55,7 @@ class ds_topk_plan(ctypes.Structure):
     _fields_ = [("segments", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("tiles_per_chunk", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("segment_vectors", ctypes.c_int32), ("tiles_per_segment", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64), ("publish_capacity", ctypes.c_int32)]
 
 
 class ds_topk_options(ctypes.Structure):
@@ -94,6 +94,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk_plan_for.argtypes = [ci, i64, i64, i64, i32, ci, ci, ctypes.POINTER(ds_topk_plan)]
     lib.ds_topk_set_overrides.restype = None
     lib.ds_topk_set_overrides.argtypes = [i32, ctypes.c_uint32, i32]
+    lib.ds_topk_release_stream.restype = ci
+    lib.ds_topk_release_stream.argtypes = [vp]
     lib.ds_topk_version.restype = ci
     lib.ds_topk_version.argtypes = []
     if path is None:
@@ -157,7 +159,12 @@ DS_TOPK_FORCE_BITONIC = 1
 
 
 def ds_topk_set_overrides(segments: int = 0, tile_seed: int = 0, flags: int = 0) -> None:
+    """Overrides for the calling thread's calls (tests and measurements)."""
     load_library().ds_topk_set_overrides(segments, tile_seed, flags)
+
+
+def ds_topk_release_stream(stream: Optional[int]) -> int:
+    return load_library().ds_topk_release_stream(stream)
 
 
 def ds_topk_version() -> int:
@@ -244,6 +251,20 @@ def topk(x: torch.Tensor, k: int, *, sorted_index: bool = False, return_value: b
     return val, idx
 
 
+def _check_out(x: torch.Tensor, batch: int, k: int, val: Optional[torch.Tensor], idx: torch.Tensor,
+               return_value: bool) -> None:
+    """Preallocated outputs must be what the kernels write: contiguous
+    (batch, k) tensors on x's device, indices int32/int64, values in x's
+    dtype (when values are returned)."""
+    def ok(t):
+        return (isinstance(t, torch.Tensor) and tuple(t.shape) == (batch, k) and t.is_contiguous()
+                and t.device == x.device)
+    if not ok(idx) or idx.dtype not in _INDEX_BYTES:
+        raise ValueError("out indices must be a contiguous (%d, %d) int32 or int64 tensor on %s" % (batch, k, x.device))
+    if return_value and (not ok(val) or val.dtype != x.dtype):
+        raise ValueError("out values must be a contiguous (%d, %d) %s tensor on %s" % (batch, k, x.dtype, x.device))
+
+
 def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: bool = False,
                return_value: bool = True, n: Optional[int] = None,
                out: Optional[Tuple[Optional[torch.Tensor], torch.Tensor]] = None, sorted_value: bool = False,
@@ -258,6 +279,7 @@ def topk_async(x: torch.Tensor, k: int, status: torch.Tensor, *, sorted_index: b
     x, dt, batch, n, row_stride = _marshal(x, k, n)
     if out is not None:
         val, idx = out
+        _check_out(x, batch, k, val, idx, return_value)
         indices_type = idx.dtype
     else:
         idx = torch.empty((batch, k), dtype=indices_type, device=x.device)

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "ds_topk.h"
 #include "sample_kernels.hpp"
@@ -41,6 +42,9 @@ constexpr int kChunkF32 = DS_TOPK_TILES_PER_CHUNK_F32;
 constexpr int kChunkBf16 = DS_TOPK_TILES_PER_CHUNK_BF16;
 constexpr int kChunkBf16BigK = DS_TOPK_TILES_PER_CHUNK_BF16_BIGK;
 constexpr int64_t kMaxGridWG = 1 << 22;  // workgroups per launch (grid x 512 threads < 2^32)
+// (row, segment) slots per launch of a split plan: bounds its workspace
+// (at most 2048 x 9216 candidates x 8 bytes, 151 MB, at k = 4096).
+constexpr int64_t kMaxSplitSlots = 2048;
 
 thread_local std::string g_err;
 
@@ -54,15 +58,20 @@ int fail(int status, const char* fmt, ...) {
     return status;
 }
 
-std::atomic<int32_t> g_force_segs{0};
-std::atomic<uint32_t> g_tile_seed{0x2545F491u};
-std::atomic<int32_t> g_flags{0};
+// Test and measurement overrides (ds_topk_set_overrides), per calling thread.
+constexpr uint32_t kDefaultTileSeed = 0x2545F491u;
+thread_local int32_t g_force_segs = 0;
+thread_local uint32_t g_tile_seed = kDefaultTileSeed;
+thread_local int32_t g_flags = 0;
+
+#ifdef DSTK_TIMING
+uint64_t* g_timing = nullptr;  // measurement build: phase timestamps of the next launches
+#endif
 
 struct Plan {
     int eb = 0;     // element bytes
     int wg = 512;   // threads per workgroup
     int vpt = 1;    // tiles per chunk (16-byte loads in flight per thread)
-    int depth = 2;  // tiles in flight beyond the one being filtered
     int cap = 0;    // LDS candidate capacity
     int pub_cap = 0;  // candidates a segment may publish
     int segs = 1;
@@ -90,18 +99,27 @@ int validate(int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k)
     return DS_OK;
 }
 
+int64_t al256(int64_t b) { return ((b + 255) / 256) * 256; }
+
+// Bytes of the split-row workspace for `rows` rows of `segs` segments that
+// publish at most `per` entries each: tickets, per-segment metadata (four
+// u64), per-segment digit directories, lists.
+int64_t split_ws_bytes(int64_t rows, int segs, int32_t per) {
+    const int64_t slots = rows * segs;
+    return al256(rows * 4) + al256(slots * 32) + al256(slots * 4 * dstk::kBins) + al256(slots * (int64_t)per * 8);
+}
+
 int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     pl->eb = dtype == DS_DTYPE_BF16 ? 2 : 4;
     const int epv = 16 / pl->eb;
     pl->wg = 512;
-    pl->depth = 0;
     pl->cap = k <= 1024 ? 8192 : 16384;
     // 16-byte loads in flight per thread (one chunk)
     pl->vpt = pl->eb == 4 ? kChunkF32 : pl->cap == 8192 ? kChunkBf16 : kChunkBf16BigK;
     pl->pub_cap = 2 * k + 1024 < pl->cap ? 2 * k + 1024 : pl->cap;
     pl->n_vec = (int)((n + epv - 1) / epv);
     int64_t s;
-    const int32_t forced = g_force_segs.load();
+    const int32_t forced = g_force_segs;
     if (forced > 0) {
         s = forced;
     } else {
@@ -119,16 +137,14 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
     pl->seg_vecs = (int)((pl->n_vec + s - 1) / s);
     pl->segs = (pl->n_vec + pl->seg_vecs - 1) / pl->seg_vecs;
     pl->tiles = (pl->seg_vecs + pl->wg - 1) / pl->wg;
-    const int64_t max_rows = kMaxGridWG / pl->segs;
-    pl->rows_per_launch = batch < max_rows ? batch : max_rows;
-    const int64_t r = pl->rows_per_launch;
-    pl->ws_bytes = 256 + 256;  // NaN word
+    int64_t max_rows = kMaxGridWG / pl->segs;
     if (pl->segs > 1) {
-        pl->ws_bytes += ((r * 4 + 255) / 256) * 256;                          // tickets
-        pl->ws_bytes += ((r * pl->segs * 32 + 255) / 256) * 256;              // segment metadata
-        pl->ws_bytes += ((r * pl->segs * 4 * dstk::kBins + 255) / 256) * 256;  // digit directories
-        pl->ws_bytes += ((r * pl->segs * (int64_t)pl->pub_cap * 8 + 255) / 256) * 256;  // candidates
+        const int64_t by_ws = kMaxSplitSlots / pl->segs;  // bounds the split workspace
+        max_rows = by_ws < max_rows ? by_ws : max_rows;
+        if (max_rows < 1) max_rows = 1;
     }
+    pl->rows_per_launch = batch < max_rows ? batch : max_rows;
+    pl->ws_bytes = pl->segs > 1 ? split_ws_bytes(pl->rows_per_launch, pl->segs, pl->pub_cap) : 0;
     return DS_OK;
 }
 
@@ -136,22 +152,27 @@ int make_plan(int dtype, int64_t batch, int64_t n, int32_t k, Plan* pl) {
 // forces a segment count; value order there holds up to kSmallValueMax.
 constexpr int64_t kSmallRows = dstk::kSmallWG / dstk::kWave;  // rows per workgroup
 bool use_small(int64_t n, int32_t k, int sorted_index) {
-    return n <= dstk::kSmallN && g_force_segs.load() == 0 &&
+    return n <= dstk::kSmallN && g_force_segs == 0 &&
            !(sorted_index == DS_ORDER_VALUE && k > dstk::kSmallValueMax);
 }
 
 // ------------------------------------------------------------------ workspace
+// One per (device, stream).  A block that has been handed to kernels is
+// never freed while the process runs (queued work, or a graph captured on
+// the stream, may still use it); growth allocates a larger block, clears it
+// with an ordered memset on the stream and retires the old one.
 struct Workspace {
     std::mutex mu;
     int device = -1;
     uint8_t* base = nullptr;
     int64_t rows = 0, slots = 0, cands = 0;
-    int32_t* nan_word = nullptr;
     uint32_t* ticket = nullptr;
     uint64_t* meta = nullptr;
     uint32_t* dir = nullptr;
     uint64_t* cand = nullptr;
-    int32_t* host_word = nullptr;  // pinned
+    std::vector<uint8_t*> retired;
+    int32_t* host_word = nullptr;      // pinned: NaN status of synchronous calls
+    int32_t* host_word_dev = nullptr;  // its device address
     int32_t epoch = 0;
 };
 
@@ -162,53 +183,72 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Make sure ws can hold `rows` rows of `segs` segments of `per` entries.
-int ensure(Workspace* ws, int64_t rows, int segs, int32_t per) {
-    const int64_t need_rows = segs > 1 ? rows : 0;
-    const int64_t need_slots = segs > 1 ? rows * segs : 0;
-    const int64_t need_cands = segs > 1 ? rows * segs * (int64_t)per : 0;
-    if (ws->base && need_rows <= ws->rows && need_slots <= ws->slots && need_cands <= ws->cands) return DS_OK;
-    hipError_t e;
-    if (!ws->host_word) {
-        e = hipHostMalloc((void**)&ws->host_word, sizeof(int32_t), hipHostMallocDefault);
-        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+int capturing(hipStream_t s, bool* yes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    *yes = cs != hipStreamCaptureStatusNone;
+    return DS_OK;
+}
+
+int ensure_host_word(Workspace* ws) {
+    if (ws->host_word) return DS_OK;
+    int32_t* h = nullptr;
+    hipError_t e = hipHostMalloc((void**)&h, 256, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    int32_t* d = nullptr;
+    e = hipHostGetDevicePointer((void**)&d, h, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(h);
+        return hip_fail(e, "hipHostGetDevicePointer");
     }
-    const int64_t rows2 = need_rows > ws->rows ? need_rows : ws->rows;
+    *h = 0;
+    ws->host_word = h;
+    ws->host_word_dev = d;
+    ws->epoch = 0;
+    return DS_OK;
+}
+
+// Make sure ws can hold `rows` rows of `segs` segments of `per` entries.
+int ensure(Workspace* ws, int64_t rows, int segs, int32_t per, hipStream_t stream) {
+    int st = ensure_host_word(ws);
+    if (st) return st;
+    if (segs <= 1) return DS_OK;
+    const int64_t need_slots = rows * segs;
+    const int64_t need_cands = rows * segs * (int64_t)per;
+    if (ws->base && rows <= ws->rows && need_slots <= ws->slots && need_cands <= ws->cands) return DS_OK;
+    bool cap_on = false;
+    st = capturing(stream, &cap_on);
+    if (st) return st;
+    if (cap_on)
+        return fail(DS_ERR_HIP, "the workspace of this stream must grow, which cannot be captured; make one "
+                                "uncaptured call of the largest shape on the stream first");
+    const int64_t rows2 = rows > ws->rows ? rows : ws->rows;
     const int64_t slots2 = need_slots > ws->slots ? need_slots : ws->slots;
     const int64_t cands2 = need_cands > ws->cands ? need_cands : ws->cands;
-    auto al = [](int64_t b) { return ((b + 255) / 256) * 256; };
-    const int64_t bytes = 256 + al(rows2 * 4) + al(slots2 * 32) + al(slots2 * 4 * dstk::kBins) + al(cands2 * 8);
-    if (ws->base) {
-        // Earlier calls may still be queued on this stream: let them finish.
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        e = hipFree(ws->base);
-        ws->base = nullptr;
-        if (e != hipSuccess) return hip_fail(e, "hipFree");
-    }
-    e = hipMalloc((void**)&ws->base, (size_t)bytes);
+    const int64_t bytes = al256(rows2 * 4) + al256(slots2 * 32) + al256(slots2 * 4 * dstk::kBins) + al256(cands2 * 8);
+    uint8_t* nb = nullptr;
+    hipError_t e = hipMalloc((void**)&nb, (size_t)bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    // tickets start at zero; ordered before the kernels on this stream
+    e = hipMemsetAsync(nb, 0, (size_t)bytes, stream);
     if (e != hipSuccess) {
-        ws->base = nullptr;
-        ws->rows = ws->slots = ws->cands = 0;
-        return hip_fail(e, "hipMalloc(workspace)");
+        (void)hipFree(nb);
+        return hip_fail(e, "hipMemsetAsync(workspace)");
     }
-    e = hipMemset(ws->base, 0, (size_t)bytes);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
-    uint8_t* p = ws->base;
-    ws->nan_word = (int32_t*)p;
-    p += 256;
+    if (ws->base) ws->retired.push_back(ws->base);
+    uint8_t* p = nb;
     ws->ticket = (uint32_t*)p;
-    p += al(rows2 * 4);
+    p += al256(rows2 * 4);
     ws->meta = (uint64_t*)p;
-    p += al(slots2 * 32);
+    p += al256(slots2 * 32);
     ws->dir = (uint32_t*)p;
-    p += al(slots2 * 4 * dstk::kBins);
+    p += al256(slots2 * 4 * dstk::kBins);
     ws->cand = (uint64_t*)p;
+    ws->base = nb;
     ws->rows = rows2;
     ws->slots = slots2;
     ws->cands = cands2;
-    ws->epoch = 0;
     return DS_OK;
 }
 
@@ -241,49 +281,18 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
     return launch_one<2, 512, kChunkBf16BigK, 16384>(prm, grid, s);
 }
 
-int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
-        int return_value, void* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream,
-        const int32_t* lengths = nullptr, int index_bytes = 4) {
-    g_err.clear();
-    int st = validate(dtype, batch, n, row_stride, k);
-    if (st) return st;
-    if (sorted_index < DS_ORDER_NONE || sorted_index > DS_ORDER_VALUE)
-        return fail(DS_ERR_INVALID_ARGUMENT, "sorted_index %d is not a ds_topk_order", sorted_index);
-    if (index_bytes != 4 && index_bytes != 8)
-        return fail(DS_ERR_INVALID_ARGUMENT, "index_bytes %d is neither 4 nor 8", index_bytes);
-    if (!in) return fail(DS_ERR_INVALID_ARGUMENT, "in is NULL");
-    if (!out_idx) return fail(DS_ERR_INVALID_ARGUMENT, "out_idx is NULL");
-    if (return_value && !out_val) return fail(DS_ERR_INVALID_ARGUMENT, "return_value set but out_val is NULL");
-    if (((uintptr_t)in) % 16 != 0) return fail(DS_ERR_MISALIGNED, "in is not 16-byte aligned");
-    if (batch == 0) return DS_OK;
-    Plan pl;
-    make_plan(dtype, batch, n, k, &pl);
+// Checks the arguments and enqueues the selection on `stream`; a NaN makes
+// the kernels store flag_value into *flag.
+int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+            int return_value, void* out_idx, void* out_val, Workspace* ws, int32_t* flag, int32_t flag_value,
+            hipStream_t stream, const int32_t* lengths, int index_bytes, const Plan& pl) {
     const bool small = use_small(n, k, sorted_index);
-
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    Workspace* ws = workspace_for(dev, stream);
-    std::lock_guard<std::mutex> g(ws->mu);
-    st = ensure(ws, pl.rows_per_launch, pl.segs, pl.pub_cap);
+    int st = ensure(ws, pl.rows_per_launch, small ? 1 : pl.segs, pl.pub_cap, stream);
     if (st) return st;
-
-    int32_t* flag = status_dev;
-    int32_t flag_value = DS_ERR_NAN;
-    if (!status_dev) {
-        if (ws->epoch >= 0x7FFFFFF0) {
-            e = hipMemsetAsync(ws->nan_word, 0, sizeof(int32_t), stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
-            ws->epoch = 0;
-        }
-        flag = ws->nan_word;
-        flag_value = ++ws->epoch;
-    }
-
     const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
     for (int64_t r0 = 0; r0 < batch; r0 += pl.rows_per_launch) {
         const int64_t rows = batch - r0 < pl.rows_per_launch ? batch - r0 : pl.rows_per_launch;
-        dstk::Params prm;
+        dstk::Params prm{};
         prm.in = (const uint8_t*)in + r0 * row_stride * es;
         prm.row_stride_bytes = row_stride * es;
         prm.n = (int32_t)n;
@@ -291,7 +300,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.segs = pl.segs;
         prm.seg_vecs = pl.seg_vecs;
         prm.n_vec = pl.n_vec;
-        prm.seed = g_tile_seed.load();
+        prm.seed = g_tile_seed;
         prm.sorted = sorted_index;
         prm.retval = return_value ? 1 : 0;
         prm.out_idx = (uint8_t*)out_idx + r0 * k * index_bytes;
@@ -299,12 +308,16 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         prm.ws_cand = ws->cand;
         prm.ws_meta = ws->meta;
         prm.ws_dir = ws->dir;
-        prm.pub_cap = pl.pub_cap;
         prm.ws_ticket = ws->ticket;
+        prm.pub_cap = pl.pub_cap;
         prm.flag = flag;
         prm.flag_value = flag_value;
-        prm.flags = (g_flags.load() & dstk::kFlagBitonic) | (index_bytes == 8 ? dstk::kFlagIdx64 : 0);
+        prm.flags = (g_flags & dstk::kFlagBitonic) | (index_bytes == 8 ? dstk::kFlagIdx64 : 0);
         prm.lengths = lengths ? lengths + r0 : nullptr;
+#ifdef DSTK_TIMING
+        prm.timing = g_timing;
+#endif
+        hipError_t e;
         if (small) {
             const int64_t grid = (rows + kSmallRows - 1) / kSmallRows;
             if (dtype == DS_DTYPE_BF16)
@@ -319,27 +332,77 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         }
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
     }
-    if (status_dev) return DS_OK;
+    return DS_OK;
+}
 
-    e = hipMemcpyAsync(ws->host_word, ws->nan_word, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
+int check_args(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+               int return_value, const void* out_idx, const void* out_val, int index_bytes) {
+    int st = validate(dtype, batch, n, row_stride, k);
+    if (st) return st;
+    if (sorted_index < DS_ORDER_NONE || sorted_index > DS_ORDER_VALUE)
+        return fail(DS_ERR_INVALID_ARGUMENT, "sorted_index %d is not a ds_topk_order", sorted_index);
+    if (index_bytes != 4 && index_bytes != 8)
+        return fail(DS_ERR_INVALID_ARGUMENT, "index_bytes %d is neither 4 nor 8", index_bytes);
+    if (!in) return fail(DS_ERR_INVALID_ARGUMENT, "in is NULL");
+    if (!out_idx) return fail(DS_ERR_INVALID_ARGUMENT, "out_idx is NULL");
+    if (return_value && !out_val) return fail(DS_ERR_INVALID_ARGUMENT, "return_value set but out_val is NULL");
+    if (((uintptr_t)in) % 16 != 0) return fail(DS_ERR_MISALIGNED, "in is not 16-byte aligned");
+    return DS_OK;
+}
+
+// The next status value a synchronous call on ws waits for (NaN reports
+// store it into the pinned host word).  Only synchronous calls use the word,
+// and each waits for its kernels, so none is in flight here.
+int32_t next_epoch(Workspace* ws) {
+    if (ws->epoch >= 0x7FFFFFF0) {
+        *(volatile int32_t*)ws->host_word = 0;
+        ws->epoch = 0;
+    }
+    return ++ws->epoch;
+}
+
+int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+        int return_value, void* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream,
+        const int32_t* lengths = nullptr, int index_bytes = 4) {
+    g_err.clear();
+    int st = check_args(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, index_bytes);
+    if (st) return st;
+    if (batch == 0) return DS_OK;
+    Plan pl;
+    make_plan(dtype, batch, n, k, &pl);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    Workspace* ws = workspace_for(dev, stream);
+    std::lock_guard<std::mutex> g(ws->mu);
+    st = ensure_host_word(ws);
+    if (st) return st;
+    int32_t* flag = status_dev;
+    int32_t flag_value = DS_ERR_NAN;
+    if (!status_dev) {
+        flag = ws->host_word_dev;
+        flag_value = next_epoch(ws);
+    }
+    st = enqueue(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, ws, flag, flag_value,
+                 stream, lengths, index_bytes, pl);
+    if (st || status_dev) return st;
     e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    if (*ws->host_word == flag_value) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
+    if (*(volatile int32_t*)ws->host_word == flag_value) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
     return DS_OK;
 }
 
 // ------------------------------------------------------------------ sampling
-// Per-(device, stream) buffers of the value-ordered top-k that sampling reads.
-struct SampleWs {
+// Per-(device, stream) buffers of the value-ordered top-k that sampling reads
+// (grown like the workspace: never freed while the process runs).
+struct SampleBuf {
     std::mutex mu;
     void* buf = nullptr;  // idx [rows][k] int32, then values [rows][k]
     int64_t bytes = 0;
-    int32_t* status = nullptr;
-    int32_t* host_word = nullptr;  // pinned
+    std::vector<void*> retired;
 };
-std::mutex g_sws_mu;
-std::map<std::pair<int, hipStream_t>, std::unique_ptr<SampleWs>> g_sws;
+std::mutex g_sbuf_mu;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<SampleBuf>> g_sbuf;
 
 int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
            const float* temperature, const float* top_p, const float* uniform, int32_t* out_token,
@@ -354,41 +417,40 @@ int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stri
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    SampleWs* sw;
+    SampleBuf* sb;
     {
-        std::lock_guard<std::mutex> g(g_sws_mu);
-        auto& slot = g_sws[std::make_pair(dev, stream)];
-        if (!slot) slot.reset(new SampleWs());
-        sw = slot.get();
+        std::lock_guard<std::mutex> g(g_sbuf_mu);
+        auto& slot = g_sbuf[std::make_pair(dev, stream)];
+        if (!slot) slot.reset(new SampleBuf());
+        sb = slot.get();
     }
-    std::lock_guard<std::mutex> g(sw->mu);
+    std::lock_guard<std::mutex> g(sb->mu);
     const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
-    const int64_t idx_bytes = ((batch * k * 4 + 255) / 256) * 256;
+    const int64_t idx_bytes = al256(batch * k * 4);
     const int64_t need = idx_bytes + batch * k * es;
-    if (!sw->status) {
-        e = hipMalloc((void**)&sw->status, 256);
-        if (e != hipSuccess) return hip_fail(e, "hipMalloc(sample status)");
-        e = hipHostMalloc((void**)&sw->host_word, sizeof(int32_t), hipHostMallocDefault);
-        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
-    }
-    if (need > sw->bytes) {
-        if (sw->buf) {
-            e = hipDeviceSynchronize();  // earlier calls on this stream may still read it
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            e = hipFree(sw->buf);
-            sw->buf = nullptr;
-            sw->bytes = 0;
-            if (e != hipSuccess) return hip_fail(e, "hipFree");
-        }
-        e = hipMalloc(&sw->buf, (size_t)need);
+    if (need > sb->bytes) {
+        bool cap_on = false;
+        st = capturing(stream, &cap_on);
+        if (st) return st;
+        if (cap_on) return fail(DS_ERR_HIP, "the sampling buffer of this stream must grow, which cannot be captured");
+        void* nb = nullptr;
+        e = hipMalloc(&nb, (size_t)need);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(sample buffers)");
-        sw->bytes = need;
+        if (sb->buf) sb->retired.push_back(sb->buf);
+        sb->buf = nb;
+        sb->bytes = need;
     }
-    int32_t* cidx = (int32_t*)sw->buf;
-    void* cval = (uint8_t*)sw->buf + idx_bytes;
-    e = hipMemsetAsync(sw->status, 0, sizeof(int32_t), stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
-    st = run(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, sw->status, stream);
+    int32_t* cidx = (int32_t*)sb->buf;
+    void* cval = (uint8_t*)sb->buf + idx_bytes;
+    Plan pl;
+    make_plan(dtype, batch, n, k, &pl);
+    Workspace* ws = workspace_for(dev, stream);
+    std::lock_guard<std::mutex> g2(ws->mu);
+    st = ensure_host_word(ws);
+    if (st) return st;
+    const int32_t flag_value = next_epoch(ws);
+    st = enqueue(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, ws, ws->host_word_dev, flag_value,
+                 stream, nullptr, 4, pl);
     if (st) return st;
     if (dtype == DS_DTYPE_BF16)
         hipLaunchKernelGGL(dssample::sample_rows<uint16_t>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
@@ -398,11 +460,59 @@ int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stri
                            (const float*)cval, cidx, k, temperature, top_p, uniform, out_token);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "sample launch");
-    e = hipMemcpyAsync(sw->host_word, sw->status, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
     e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    if (*sw->host_word == DS_ERR_NAN) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
+    if (*(volatile int32_t*)ws->host_word == flag_value) return fail(DS_ERR_NAN, "a row holds NaN in columns [0, n)");
+    return DS_OK;
+}
+
+// Releases the workspace and sampling buffers of (current device, stream)
+// after waiting for the stream.
+int release(hipStream_t stream) {
+    g_err.clear();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    std::unique_ptr<Workspace> w;
+    std::unique_ptr<SampleBuf> b;
+    {
+        std::lock_guard<std::mutex> g(g_ws_mu);
+        auto it = g_ws.find(std::make_pair(dev, stream));
+        if (it != g_ws.end()) {
+            w = std::move(it->second);
+            g_ws.erase(it);
+        }
+    }
+    {
+        std::lock_guard<std::mutex> g(g_sbuf_mu);
+        auto it = g_sbuf.find(std::make_pair(dev, stream));
+        if (it != g_sbuf.end()) {
+            b = std::move(it->second);
+            g_sbuf.erase(it);
+        }
+    }
+    hipError_t first = hipSuccess;
+    auto fr = [&](void* p) {
+        const hipError_t x = hipFree(p);
+        if (x != hipSuccess && first == hipSuccess) first = x;
+    };
+    if (w) {
+        std::lock_guard<std::mutex> g(w->mu);
+        if (w->base) fr(w->base);
+        for (uint8_t* p : w->retired) fr(p);
+        if (w->host_word) {
+            const hipError_t x = hipHostFree(w->host_word);
+            if (x != hipSuccess && first == hipSuccess) first = x;
+        }
+    }
+    if (b) {
+        std::lock_guard<std::mutex> g(b->mu);
+        if (b->buf) fr(b->buf);
+        for (void* p : b->retired) fr(p);
+    }
+    if (first != hipSuccess) return hip_fail(first, "hipFree");
     return DS_OK;
 }
 
@@ -469,11 +579,10 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
     if (!plan) return fail(DS_ERR_INVALID_ARGUMENT, "plan is NULL");
     Plan pl;
     make_plan(dtype, batch, n, k, &pl);
+    std::memset(plan, 0, sizeof *plan);
     if (use_small(n, k, sorted_index)) {
-        std::memset(plan, 0, sizeof *plan);
         plan->threads = dstk::kSmallWG;
         plan->grid = (batch + kSmallRows - 1) / kSmallRows;
-        plan->workspace_bytes = 256;
         return DS_OK;
     }
     plan->segments = pl.segs;
@@ -484,14 +593,23 @@ int ds_topk_plan_for(int dtype, int64_t batch, int64_t n, int64_t row_stride, in
     plan->tiles_per_segment = pl.tiles;
     plan->grid = pl.rows_per_launch * pl.segs;
     plan->workspace_bytes = pl.ws_bytes;
+    plan->publish_capacity = pl.segs > 1 ? pl.pub_cap : 0;
     return DS_OK;
 }
 
 void ds_topk_set_overrides(int32_t segments, uint32_t tile_seed, int32_t flags) {
-    g_force_segs.store(segments > 0 ? segments : 0);
-    g_tile_seed.store(tile_seed ? tile_seed : 0x2545F491u);
-    g_flags.store(flags & DS_TOPK_FORCE_BITONIC);
+    g_force_segs = segments > 0 ? segments : 0;
+    g_tile_seed = tile_seed ? tile_seed : kDefaultTileSeed;
+    g_flags = flags & DS_TOPK_FORCE_BITONIC;
 }
+
+int ds_topk_release_stream(void* stream) { return release((hipStream_t)stream); }
+
+#ifdef DSTK_TIMING
+// Measurement build only: the next launches note their phase timestamps in
+// buf[grid][16] (null: stop).
+void ds_topk_timing_buffer(uint64_t* buf) { g_timing = buf; }
+#endif
 
 int ds_topk_version(void) { return kVersion; }
 
