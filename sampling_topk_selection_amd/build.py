@@ -16,6 +16,9 @@ SRC = os.path.join(HERE, "csrc", "ds_topk.hip")
 DEPS = [SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
         os.path.join(ROOT, "include", "ds_topk.h")]
 LIB = os.path.join(HERE, "libds_topk.so")
+# Measurement build of the same sources: the kernels also note phase
+# timestamps (DSTK_TIMING); read by sampling_topk_selection_amd.phases.
+TIMING_LIB = os.path.join(HERE, "libds_topk_timing.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
 CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 
@@ -59,10 +62,10 @@ def stale(lib: str = LIB, deps=None) -> bool:
     return any(os.path.getmtime(d) > t for d in deps)
 
 
-def _hipcc(src: str, lib: str, verbose: bool) -> None:
+def _hipcc(src: str, lib: str, verbose: bool, extra=()) -> None:
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                             "-o", tmp, src]
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+                                           "-o", tmp, src]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:
@@ -72,13 +75,16 @@ def _hipcc(src: str, lib: str, verbose: bool) -> None:
     os.replace(tmp, lib)
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    """Build libds_topk.so (the library) and libds_calib.so (benchmark
-    calibration kernels)."""
+def build(force: bool = True, verbose: bool = False, timing: bool = True) -> str:
+    """Build libds_topk.so (the library), libds_calib.so (benchmark
+    calibration kernels) and, with `timing`, libds_topk_timing.so (the
+    library with phase timestamps, for measurement only)."""
     if force or stale():
         _hipcc(SRC, LIB, verbose)
     if force or stale(CALIB_LIB, [CALIB_SRC]):
         _hipcc(CALIB_SRC, CALIB_LIB, verbose)
+    if timing and (force or stale(TIMING_LIB)):
+        _hipcc(SRC, TIMING_LIB, verbose, ["-DDSTK_TIMING"])
     return LIB
 
 

@@ -44,6 +44,12 @@ namespace dstk {
 
 using u32 = uint32_t;
 using u64 = uint64_t;
+// A pointer to global memory in the compiler's address space 1: accesses
+// are plain global_* instructions.  (A generic pointer whose origin the
+// compiler cannot see becomes flat_* accesses, which also count against
+// the LDS wait counter, so every LDS wait would wait for them too.)
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
 // One 16-byte vector as the hardware loads it: kept whole in registers (a
 // four-register tuple), so a load's destination is the register the scan
 // reads, also across loop iterations.
@@ -174,16 +180,16 @@ constexpr int kOrderValue = 2;   // Params::sorted: largest composite first
 
 // Where a row's column indices go: int32 or int64 elements.
 struct IdxOut {
-    void* p;
+    gptr<void> p;
     int i64;
     __device__ __forceinline__ void put(u32 pos, u32 col) const {
         if (i64)
-            ((int64_t*)p)[pos] = (int64_t)col;
+            ((gptr<int64_t>)p)[pos] = (int64_t)col;
         else
-            ((int32_t*)p)[pos] = (int32_t)col;
+            ((gptr<int32_t>)p)[pos] = (int32_t)col;
     }
     __device__ __forceinline__ IdxOut at(u64 pos) const {
-        return IdxOut{(void*)((uint8_t*)p + pos * (i64 ? 8u : 4u)), i64};
+        return IdxOut{(gptr<void>)((gptr<uint8_t>)p + pos * (i64 ? 8u : 4u)), i64};
     }
 };
 
@@ -221,21 +227,47 @@ struct Smem {
     u32 lwfirst[16];     // block_locate: per-wave highest non-empty bin (waves with any)
     u64 trash[64];       // scan: written by the lanes that append nothing
     u32 tbase[512];      // emit: per-thread base rank in the column bitmap
-#ifdef DSTK_PROBE_SLOTS
-    u64 probe_ts[DSTK_PROBE_SLOTS];  // instrumentation builds only
+#ifdef DSTK_TIMING
+    u64 ts[16];          // phase timestamps (measurement build only)
 #endif
 };
 
-// Optional instrumentation hook (phase timestamps); compiled out by default.
-#ifndef DSTK_PHASE
-#define DSTK_PHASE(i) ((void)0)
+// Phase timestamps, compiled in only by the measurement build (DSTK_TIMING):
+// thread 0 notes the constant 100 MHz clock at the points below, and a
+// workgroup copies its notes to Params::timing[blockIdx.x][kTimingSlots]
+// where it ends.  Unvisited points stay 0.
+enum Phase : int {
+    kPhStart = 0,     // kernel entry
+    kPhSeed,          // seed bound located
+    kPhScan,          // last chunk appended
+    kPhSync,          // candidates converted and counted
+    kPhLocate,        // bin of the segment's k-th entry located (split rows: and the directory written)
+    kPhExchange,      // (unused)
+    kPhPublish,       // candidates stored (split rows)
+    kPhTicket,        // ticket taken (split rows)
+    kPhHeaders,       // merger: metadata and directory heads read
+    kPhLoad,          // merger: row histogram, row bin and shares worked out
+    kPhMergeLocate,   // merger: the lists' needed prefixes loaded
+    kPhRefine,        // exact k-th composite found
+    kPhEmit,          // outputs written
+    kTimingSlots = 16
+};
+#ifdef DSTK_TIMING
+#define DSTK_T(sm, id)                                     \
+    do {                                                   \
+        if (threadIdx.x == 0) (sm).ts[id] = wall_clock64(); \
+    } while (0)
+#define DSTK_T_FLUSH(sm, timing)                                                      \
+    do {                                                                              \
+        if (threadIdx.x == 0 && (timing))                                             \
+            for (int i_ = 0; i_ < kTimingSlots; ++i_)                                 \
+                (timing)[(uint64_t)blockIdx.x * kTimingSlots + i_] = (sm).ts[i_];     \
+    } while (0)
+#else
+#define DSTK_T(sm, id) ((void)0)
+#define DSTK_T_FLUSH(sm, timing) ((void)0)
 #endif
-#ifndef DSTK_PROBE_INIT
-#define DSTK_PROBE_INIT
-#endif
-#ifndef DSTK_PROBE_FLUSH
-#define DSTK_PROBE_FLUSH() ((void)0)
-#endif
+
 // Ends the wave where the last output of a workgroup is written (nothing
 // follows it on any path; a return from an out-of-line caller would first
 // reload the registers that caller saved).
@@ -336,13 +368,37 @@ __device__ __forceinline__ u64 wave_max64(u64 v) {
 // the device-coherent level, loads do not hit a stale L2 line.  Data handed
 // from one workgroup to another goes through these, so the hand-off needs no
 // release fence (which would write back the whole L2).
-template <class T>
-__device__ __forceinline__ void st_agent(T* p, T v) {
+template <class P, class T>
+__device__ __forceinline__ void st_agent(P p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+template <class P>
+__device__ __forceinline__ auto ld_agent(P p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A uniform value as an opaque register value.  Values loaded from the
+// kernel-argument segment count as free to reload for the register
+// allocator; under SGPR pressure it reloads them inside loops (a scalar
+// load and a wait per use).  After this empty asm the value is an ordinary
+// one that it keeps, or spills to a VGPR lane (one v_readlane).
 template <class T>
-__device__ __forceinline__ T ld_agent(const T* p) {
-    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ T keep(T x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+// The same for a pointer to global memory, kept as one.
+template <class T>
+__device__ __forceinline__ gptr<T> keep_g(T* x) {
+    uint64_t v = (uint64_t)(uintptr_t)x;
+    asm volatile("" : "+s"(v));
+    return (gptr<T>)(uintptr_t)v;
+}
+template <class T>
+__device__ __forceinline__ gptr<T> keep_g(gptr<T> x) {
+    uint64_t v = (uint64_t)(uintptr_t)x;
+    asm volatile("" : "+s"(v));
+    return (gptr<T>)(uintptr_t)v;
 }
 
 // Reserve `c` consecutive slots per lane behind *counter (one LDS atomic per
@@ -730,7 +786,7 @@ struct ColRanks {
     u32 lp;         // log2 of the words per row
     u32 pitch;      // row pitch in words
     // The words of LDS needed for n columns.
-    __device__ static u32 plan(u32 n, u32& lp, u32& pitch) {
+    __device__ static __forceinline__ u32 plan(u32 n, u32& lp, u32& pitch) {
         const u32 words = (n + 31) / 32;
         lp = 0;
         while (((u32)WG << lp) < words) ++lp;
@@ -782,12 +838,12 @@ struct ColRanks {
 // (sorted runs of one wave each and binary searches) when k fits one entry
 // per thread, else from a bitonic sort of the composites in LDS.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, void* out_idx_p,
-                     void* out_val) {
+__device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int retval, int flags, gptr<void> out_idx_p,
+                     gptr<void> out_val) {
     const IdxOut out_idx{out_idx_p, flags & kFlagIdx64};
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
-    VT* ov = (VT*)out_val;
+    const gptr<VT> ov = (gptr<VT>)out_val;
     if (!sorted) {
         for (u32 i = tid; i < k; i += WG) {
             const u64 e = sm.buf[i];
@@ -834,10 +890,8 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
                           (u32)__builtin_amdgcn_readlane((int)elo, j);
             local += o > e ? 1u : 0u;
         }
-        DSTK_PHASE(42);
         if (tid >= k) local = l;  // the zeros keep distinct slots behind the entries
         __syncthreads();          // every entry is read before the runs overwrite buf
-        DSTK_PHASE(38);
         sm.buf[wave * kWave + local] = e;
         __syncthreads();
         u32 rank = 0;
@@ -849,7 +903,6 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
             for (u32 st = kWave / 2; st > 0; st >>= 1) c += run[c + st - 1] > e ? st : 0u;
             rank += c + (run[c] > e ? 1u : 0u);
         }
-        DSTK_PHASE(39);
         __syncthreads();  // the runs are read; reorder through buf for coalesced stores
         if (tid < k) sm.buf[rank] = e;
         __syncthreads();
@@ -865,7 +918,6 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
     // padding ~0 sorts last either way.
     u32 P = 1;
     while (P < k) P <<= 1;
-    DSTK_PHASE(38);
     for (u32 i = tid; i < P; i += WG) {
         const u64 e = i < k ? sm.buf[i] : 0ull;
         sm.buf[i] = i >= k ? ~0ull : sorted == kOrderValue ? ~e : (((u64)comp_col<E>(e) << 32) | comp_key<E>(e));
@@ -893,7 +945,6 @@ __device__ __noinline__ void emit(Smem<CAP>& sm, u32 k, u32 n, int sorted, int r
         }
     }
     __syncthreads();
-    DSTK_PHASE(39);
     for (u32 i = tid; i < k; i += WG) {
         const u64 s = sm.buf[i];
         if (sorted == kOrderValue) {
@@ -920,7 +971,7 @@ __device__ __forceinline__ u64 low_mask(int b) { return b >= 64 ? ~0ull : ((1ull
 // Call from every thread; returns after a barrier, with the results visible
 // to all.  With `zero` the histogram is cleared on the way.
 template <int WG, int CAP, bool kPub = false>
-__device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero, u32* dir = nullptr) {
+__device__ __forceinline__ void block_locate(Smem<CAP>& sm, u32 r0, u32 r1, bool zero, gptr<u32> dir = nullptr) {
     constexpr u32 kPer = kBins / WG;
     constexpr u32 kW = WG / kWave;
     static_assert(kPer * WG == kBins && kW <= 16, "bins per thread");
@@ -1105,12 +1156,10 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
     }
     if constexpr (kFixedFirst) {
         __syncthreads();
-        DSTK_PHASE(20);
         block_locate<WG, CAP>(sm, r1, 0u, true);
         P |= (u64)sm.loc_digit[0] << kSh1;
         fixed = kSh1;
         r = sm.loc_r[0];
-        DSTK_PHASE(21);
         if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
         if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(kSh1), P, r);
     }
@@ -1130,7 +1179,6 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         A &= sm.red[w][1];
     }
     u64 D = (O ^ A) & low_mask(fixed);  // bits below those fixed where entries of the bin differ
-    if constexpr (!kFixedFirst) DSTK_PHASE(20);
     for (int level = 0; level < 64 / kHistBits + 2; ++level) {
         // D != 0 here: the remaining set has at least two (distinct) entries
         const int hb = 63 - __clzll((long long)D);
@@ -1172,7 +1220,6 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         const u32 d = sm.loc_digit[0], rr = sm.loc_r[0], c = sm.loc_c[0];
         P |= ((u64)(d >> len2) << lo1) | ((u64)(d & (u32)low_mask(len2)) << sh2);
         P |= A & (low_mask(lo1) & ~low_mask(hb2 + 1));  // the shared bits between the two parts
-        if constexpr (!kFixedFirst) DSTK_PHASE(21);
         fixed = sh2;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
         if constexpr (kFixedFirst)
@@ -1187,12 +1234,10 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
 // order by a bitmap behind them, or a bitonic sort).
 template <class E, int WG, int CAP>
 __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
-                                            int flags, void* out_idx_p, void* out_val) {
+                                            int flags, gptr<void> out_idx_p, gptr<void> out_val) {
     const IdxOut out_idx{out_idx_p, flags & kFlagIdx64};
-    DSTK_PHASE(40);
     __syncthreads();
     keep_at_least<WG, CAP>(sm, 0, cnt, T);
-    DSTK_PHASE(41);
     emit<E, WG, CAP>(sm, k, n, sorted, retval, flags, out_idx.p, out_val);
 }
 
@@ -1201,7 +1246,7 @@ __device__ __noinline__ void emit_compacted(Smem<CAP>& sm, u32 cnt, u64 T, u32 k
 // Returns the new count; sm.kth gets the k-th entry.
 template <int WG, int CAP, bool kPub = false>
 __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u32 b1, u32 r1, u32 c1,
-                                        u32* dir = nullptr) {
+                                        gptr<u32> dir = nullptr) {
     const u32 tid = threadIdx.x;
     __syncthreads();
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
@@ -1221,10 +1266,10 @@ __device__ __noinline__ u32 reduce_to_k(Smem<CAP>& sm, u32 cnt, u32 k, u32 q, u3
 // when no bitmap fits, compact and fall back to emit().
 template <class E, int WG, int CAP>
 __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u32 k, u32 n, int sorted, int retval,
-                                               int flags, IdxOut out_idx, void* out_val) {
+                                               int flags, IdxOut out_idx, gptr<void> out_val) {
     const u32 tid = threadIdx.x;
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
-    VT* ov = (VT*)out_val;
+    const gptr<VT> ov = (gptr<VT>)out_val;
     if (!sorted) {
         u32 mine = 0;
         for (u32 i = tid; i < cnt; i += WG) mine += sm.buf[i] >= T ? 1u : 0u;
@@ -1245,7 +1290,6 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
     u32 lp, pitch;
     const u32 need = ColRanks<WG>::plan(n, lp, pitch);
     u32* bm = nullptr;
-    DSTK_PHASE(22);
     if (sorted == kOrderIndex && !(flags & kFlagBitonic)) {
         if (need <= (u32)kHistWords) bm = sm.hist;
         else if ((u64)cnt * 2 + need <= (u64)CAP * 2) bm = (u32*)(sm.buf + cnt);
@@ -1263,11 +1307,9 @@ __device__ __forceinline__ void emit_threshold(Smem<CAP>& sm, u32 cnt, u64 T, u3
         if (e >= T) cr.mark(comp_col<E>(e));
     }
     __syncthreads();
-    DSTK_PHASE(23);
     u32 tot;
     sm.tbase[tid] = block_excl_scan<WG, CAP>(sm, cr.row_count(), &tot);
     __syncthreads();
-    DSTK_PHASE(24);
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
         if (e >= T) {
@@ -1306,7 +1348,6 @@ __device__ __forceinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
         gap[w] = w ? R - __builtin_amdgcn_readfirstlane(sm.wfill[w - 1]) : 0u;
         N += f;
     }
-    DSTK_PHASE(33);
     bool nan = false;
     constexpr u32 kB = 8;  // entries per thread and batch: one batch for most syncs
     for (u32 base = 0; base < N; base += WG * kB) {
@@ -1329,7 +1370,6 @@ __device__ __forceinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
             e[i] = compose<E>(E::key(bits), (u32)e[i]);
         }
         __syncthreads();
-        DSTK_PHASE(34);
 #pragma unroll
         for (u32 i = 0; i < kB; ++i) {
             const u32 j = base + i * WG + tid;
@@ -1339,7 +1379,6 @@ __device__ __forceinline__ u32 sync_regions(Smem<CAP>& sm, u32 cbase, u32 R) {
         __syncthreads();
     }
     if (nan) sm.nan = 1;  // benign race: every writer stores 1
-    DSTK_PHASE(35);
     return cbase + N;
 }
 
@@ -1408,7 +1447,6 @@ __device__ __forceinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R)
     const u32 fill = __builtin_amdgcn_readfirstlane(sm.wfill[wave]);
     const u32 rb = cbase + wave * R;
     bool nan = false;
-    DSTK_PHASE(36);
     constexpr u32 kU = 4;  // entries in flight per lane
     for (u32 i0 = 0; i0 < fill; i0 += kU * kWave) {
         u64 e[kU];
@@ -1428,7 +1466,6 @@ __device__ __forceinline__ void convert_regions(Smem<CAP>& sm, u32 cbase, u32 R)
         }
     }
     if (nan) sm.nan = 1;  // benign race: every writer stores 1
-    DSTK_PHASE(37);
     __syncthreads();
 }
 
@@ -1624,18 +1661,19 @@ struct Params {
     int32_t flag_value;
     int32_t flags;     // kFlag* bits
     const int32_t* lengths;  // [batch] valid columns per row (clamped to [0, n]), or null: all n
+    u64* timing;       // measurement build: [grid][kTimingSlots] phase timestamps; else unused
 };
 
 // Output slots [k, kout) of a row with only k = len < kout valid columns:
 // the columns len .. kout - 1, which act as -inf (they come after every
 // valid entry in each order), with -inf values.
 template <class E, int WG>
-__device__ __forceinline__ void write_tail(IdxOut row_idx, void* row_val, u32 k, u32 kout) {
+__device__ __forceinline__ void write_tail(IdxOut row_idx, gptr<void> row_val, u32 k, u32 kout) {
     using VT = typename std::conditional<E::kKeyBits == 16, uint16_t, uint32_t>::type;
     constexpr VT kNegInf = E::kKeyBits == 16 ? (VT)0xFF80u : (VT)0xFF800000u;
     for (u32 j = k + threadIdx.x; j < kout; j += WG) {
         row_idx.put(j, j);
-        if (row_val) ((VT*)row_val)[j] = kNegInf;
+        if (row_val) ((gptr<VT>)row_val)[j] = kNegInf;
     }
 }
 
@@ -1680,15 +1718,18 @@ struct Slot {
 // NaN report; the workgroup ends here.
 template <class E, int WG, int CAP>
 __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
-                                             int sorted, int retval, int flags, void* row_idx_p, void* row_val,
-                                             int32_t* flag, int32_t flag_value) {
+                                             int sorted, int retval, int flags, gptr<void> row_idx_p, gptr<void> row_val,
+                                             gptr<int32_t> flag, int32_t flag_value, u64* timing) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
-    DSTK_PHASE(5);
+    DSTK_T(sm, kPhRefine);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
     __syncthreads();
     if (threadIdx.x == 0 && sm.nan) *flag = flag_value;
+    DSTK_T(sm, kPhEmit);
+    DSTK_T_FLUSH(sm, timing);
+    (void)timing;
     DSTK_EXIT();
 }
 
@@ -1696,9 +1737,9 @@ __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, 
 // across segments): stream the published entries at or above the row
 // bound through the buffer, reducing to k whenever it fills.
 template <class E, int WG, int CAP>
-__device__ __noinline__ void merge_fallback(Smem<CAP>& sm, const u64* rmeta, const u32* rdir, const u64* rc, u32 S,
+__device__ __noinline__ void merge_fallback(Smem<CAP>& sm, gptr<const u64> rmeta, gptr<const u32> rdir, gptr<const u64> rc, u32 S,
                                             u32 cap, u64 Lrow, u32 k, u32 n, int sorted, int retval, int flags,
-                                            void* row_idx_p, void* row_val, int32_t* flag, int32_t flag_value) {
+                                            gptr<void> row_idx_p, gptr<void> row_val, gptr<int32_t> flag, int32_t flag_value) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u32 tid = threadIdx.x;
     const u32 dL = top_digit(Lrow);
@@ -1774,7 +1815,6 @@ void topk_rows(Params p) {
     static_assert(NV <= WG / kWave, "one wave's chunk must fit in a tile of the workgroup");
     __shared__ Smem<CAP> sm;
 
-    DSTK_PROBE_INIT
     const u32 tid = threadIdx.x;
     const u32 row = blockIdx.x / (u32)p.segs;
     const u32 seg = blockIdx.x % (u32)p.segs;
@@ -1789,8 +1829,8 @@ void topk_rows(Params p) {
     }
     const u32 k = kout < n ? kout : n;
     const uint8_t* row_in = p.in + (int64_t)row * p.row_stride_bytes;
-    const IdxOut row_idx = IdxOut{p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
-    void* const row_val = p.retval ? (void*)((uint8_t*)p.out_val + (int64_t)row * kout * EB) : nullptr;
+    const IdxOut row_idx = IdxOut{(gptr<void>)p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
+    const gptr<void> row_val = p.retval ? (gptr<void>)((gptr<uint8_t>)p.out_val + (int64_t)row * kout * EB) : nullptr;
     if (k == 0) {  // no valid column: the whole output is the -inf columns
         if (seg == 0) write_tail<E, WG>(row_idx, row_val, 0u, kout);
         return;
@@ -1829,8 +1869,11 @@ void topk_rows(Params p) {
         sm.outcount = 0;
         sm.pflag[0] = 0;
         sm.pflag[1] = 0;
+#ifdef DSTK_TIMING
+        for (int i = 0; i < kTimingSlots; ++i) sm.ts[i] = 0;
+#endif
     }
-    DSTK_PHASE(0);
+    DSTK_T(sm, kPhStart);
 
     PreFilter<E> pf;
     pf.set(0ull);
@@ -1898,14 +1941,13 @@ void topk_rows(Params p) {
             count(std::true_type{});
         else
             count(std::false_type{});
-        DSTK_PHASE(19);
         __syncthreads();
         // the locate also clears the histogram: from here on it counts
         // exactly the synced entries
         block_locate<WG, CAP>(sm, k, 0u, true);
         if (sm.loc_c[0] > 0) st.L = digit_floor(sm.loc_digit[0]);
         pf.set(st.L);
-        DSTK_PHASE(7);
+        DSTK_T(sm, kPhSeed);
     };
     // Append a chunk, then check.  After chunks 7, 15, 31, ... (a fixed
     // schedule, so every wave takes the same barriers; on long segments the
@@ -1914,11 +1956,9 @@ void topk_rows(Params p) {
     // bound: a raise there costs more than the appends it saves, and a full
     // region raises the bound anyway.
     auto process = [&](u32 t0, const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
-        if (t0 == 2 * NV) DSTK_PHASE(29);
         const u32 c = t0 / NV;
         const bool raise = t0 + NV < ntiles && c >= 7 && ((c + 1) & c) == 0;
         const u32 rtile = append_chunk<E, WG, NV, CAP>(sm, cx, st, pf, v, vb, 0u);
-        if (t0 == 2 * NV) DSTK_PHASE(30);
         const bool again = check_pending<WG, CAP>(sm, st, rtile < (u32)NV);
         if (again || raise) {
             VecBases<NV> bases;
@@ -1927,8 +1967,6 @@ void topk_rows(Params p) {
             st = rare_rounds<E, WG, NV, CAP>(sm, cx, st, bases, rtile, again);
             pf.set(st.L);
         }
-        if (t0 == 2 * NV) DSTK_PHASE(31);
-        DSTK_PHASE(25 + (c < 6u ? c : 6u));
     };
     {
         // Double buffering: chunk c + 1 is in flight while chunk c is
@@ -1957,7 +1995,15 @@ void topk_rows(Params p) {
         }
     }
     // (the last check's barrier follows every wave's last append)
-    if (p.segs == 1) {
+    DSTK_T(sm, kPhScan);
+    // the arguments the tail uses, as kept values (see keep())
+    const gptr<int32_t> flag = keep_g(p.flag);
+    const int32_t flag_value = keep(p.flag_value);
+    u64* const timing = keep(p.timing);
+    (void)timing;
+    const int sorted = keep(p.sorted), retval = keep(p.retval), flags = keep(p.flags);
+    const u32 S = keep((u32)p.segs);
+    if (S == 1) {
         const u32 c = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
         if (tid == 0) sm.count = c;
     } else {
@@ -1967,39 +2013,42 @@ void topk_rows(Params p) {
     if (st.nan) sm.nan = 1;  // benign race: every writer stores 1
     u64 L = st.L;
     if (tid == 0) sm.L = L;
-    DSTK_PHASE(1);
     __syncthreads();
-    DSTK_PHASE(9);
+    DSTK_T(sm, kPhSync);
     u32 cnt = sm.count;
     const u32 wave = tid / kWave;
 
-    if (p.segs == 1) {
+    if (S == 1) {
         block_locate<WG, CAP>(sm, k, 0u, true);
-        DSTK_PHASE(2);
-        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, kout, n, p.sorted,
-                                    p.retval, p.flags, row_idx.p, row_val, p.flag, p.flag_value);
+        DSTK_T(sm, kPhLocate);
+        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, kout, n, sorted,
+                                    retval, flags, row_idx.p, row_val, flag, flag_value, timing);
         return;
     }
 
     // ---- split row: publish this segment's live candidates (entries in the
     // bin of its k-th counted entry or above) in descending top-digit order,
     // with a directory dir[j] = number of entries with top digit >= d_hi - j.
-    const u32 S = (u32)p.segs;
     const u32 slot = row * S + seg;
+    const u32 cap = keep((u32)p.pub_cap);
+    const gptr<u64> ws_cand = keep_g(p.ws_cand);
+    const gptr<u64> ws_meta = keep_g(p.ws_meta);
+    const gptr<u32> ws_dir = keep_g(p.ws_dir);
+    const gptr<u32> ws_ticket = keep_g(p.ws_ticket);
     {
         // q = ceil(k / S): with every segment holding q entries at or above
         // its q-bound, the smallest q-bound over the row is a valid bound too
         const u32 q = (k + S - 1) / S;
-        u32* dir = p.ws_dir + (u64)slot * kBins;
+        const gptr<u32> dir = ws_dir + (u64)slot * kBins;
         // locate, directory and placement offsets in one pass over the bins
         block_locate<WG, CAP, true>(sm, k, q, false, dir);
-        DSTK_PHASE(11);
+        DSTK_T(sm, kPhLocate);
         u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
         u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
         u64 bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
         const RegionMap<WG> map(sm, st.cbase, st.R);
         bool moved = false;  // the regions have been moved together
-        if (live > (u32)p.pub_cap) {
+        if (live > cap) {
             // too many to publish: move the entries together (already
             // counted: the move alone), then reduce exactly to k
             __syncthreads();  // everyone has built the map from wfill
@@ -2012,70 +2061,66 @@ void topk_rows(Params p) {
             live = sm.loc_above[0] + sm.loc_c[0];
             bq = sm.loc_c[1] ? digit_floor(sm.loc_digit[1]) : 0ull;
         }
-        DSTK_PHASE(10);
         const u32 dh = sm.loc_dhi;
         if (tid == 0) {
-            u64* meta = p.ws_meta + (u64)slot * 4;
+            const gptr<u64> meta = ws_meta + (u64)slot * 4;
             st_agent(&meta[0], (u64)live | ((u64)dl << 32));
             st_agent(&meta[1], (u64)(live ? dh : 0u));
             st_agent(&meta[2], L);
             st_agent(&meta[3], bq);
         }
-        u64* cand = p.ws_cand + (u64)slot * (u32)p.pub_cap;
+        const gptr<u64> cand = ws_cand + (u64)slot * cap;
         const u32 total = moved ? cnt : map.total;
         for (u32 i = tid; i < total; i += WG) {
             const u64 e = sm.buf[moved ? i : map.addr(i)];
             const u32 d = top_digit(e);
             if (live > 0 && d >= dl) {
                 const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
-                if (pos < (u32)p.pub_cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
+                if (pos < cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
             }
         }
     }
-    DSTK_PHASE(2);
     // Hand-off: this wave's device-coherent stores have completed; once every
     // wave is past the barrier, one relaxed ticket increment publishes the
     // segment.  The last of the row's segments merges.
+    DSTK_T(sm, kPhPublish);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    DSTK_PHASE(12);
     if (tid == 0) {
-        const u32 prev = __hip_atomic_fetch_add(&p.ws_ticket[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u32 prev = __hip_atomic_fetch_add(&ws_ticket[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm.last = prev == S - 1;
     }
     __syncthreads();
+    DSTK_T(sm, kPhTicket);
     if (!sm.last) {
-        if (tid == 0 && sm.nan) *p.flag = p.flag_value;
-        DSTK_PHASE(3);
-        DSTK_PROBE_FLUSH();
+        if (tid == 0 && sm.nan) *flag = flag_value;
+        DSTK_T_FLUSH(sm, timing);
         return;
     }
-    DSTK_PHASE(4);
 
     // ---- merge.  Every element of the row's top-k is in some segment's
     // published list.  One round trip reads every segment's metadata and the
     // head of its directory; the row histogram, a one-wave walk to the bin of
     // the row's k-th entry and the segments' shares follow, then the shares
     // are loaded and the selection finishes as for a single segment.
-    const u32 cap = (u32)p.pub_cap;
-    const u64* rc = p.ws_cand + (u64)row * S * cap;
-    const u32* rdir = p.ws_dir + (u64)row * S * kBins;
+    const gptr<const u64> rc = ws_cand + (u64)row * S * cap;
+    const gptr<const u32> rdir = ws_dir + (u64)row * S * kBins;
     constexpr u32 kDirCache = 16;  // directory entries read with the metadata
     u64* mc = sm.buf;                                 // [S][4] metadata
     u32* dc = (u32*)(sm.buf + 4 * S);                 // [S][kDirCache] directory heads
-    for (u32 i = tid; i < S * 4; i += WG) mc[i] = ld_agent(&p.ws_meta[(u64)row * S * 4 + i]);
+    for (u32 i = tid; i < S * 4; i += WG) mc[i] = ld_agent(&ws_meta[(u64)row * S * 4 + i]);
     for (u32 i = tid; i < S * kDirCache; i += WG)
         dc[i] = ld_agent(&rdir[(u64)(i / kDirCache) * kBins + (i % kDirCache)]);
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
     if (tid == 0) {
-        p.ws_ticket[row] = 0;  // ready for the next call
+        st_agent(&ws_ticket[row], 0u);  // ready for the next call
         sm.d_hi = 0;
     }
     __syncthreads();
-    DSTK_PHASE(15);
     auto dirv = [&](u32 s_, u32 j) -> u32 {  // entries of segment s_ with digit >= d_hi - j
         return j < kDirCache ? dc[s_ * kDirCache + j] : ld_agent(&rdir[(u64)s_ * kBins + j]);
     };
+    DSTK_T(sm, kPhHeaders);
     // Row histogram of the published entries, from the directories: one
     // thread per (segment, cached directory entry), then the entries of
     // segments with more bins than the cache holds.
@@ -2119,7 +2164,6 @@ void topk_rows(Params p) {
         }
     }
     __syncthreads();
-    DSTK_PHASE(17);
     if (wave == 0) {
         // One wave walks the bins down from the highest published one to
         // the bin of the row's k-th entry (the counts at and above it are
@@ -2168,12 +2212,14 @@ void topk_rows(Params p) {
     }
     __syncthreads();
     const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0], total = sm.newtotal;
-    DSTK_PHASE(13);
+    DSTK_T(sm, kPhLoad);
     if (total > (u32)CAP) {
-        merge_fallback<E, WG, CAP>(sm, p.ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
-                                   p.sorted, p.retval,
-                                   p.flags, row_idx.p, row_val, p.flag, p.flag_value);
+        merge_fallback<E, WG, CAP>(sm, ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
+                                   sorted, retval,
+                                   flags, row_idx.p, row_val, flag, flag_value);
         if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
+        DSTK_T(sm, kPhEmit);
+        DSTK_T_FLUSH(sm, timing);
         return;
     }
     {
@@ -2202,9 +2248,9 @@ void topk_rows(Params p) {
         }
     }
     __syncthreads();
-    DSTK_PHASE(14);
-    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, kout, n, p.sorted, p.retval, p.flags, row_idx.p, row_val,
-                                p.flag, p.flag_value);
+    DSTK_T(sm, kPhMergeLocate);
+    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, kout, n, sorted, retval, flags, row_idx.p, row_val,
+                                flag, flag_value, timing);
 }
 
 }  // namespace dstk
@@ -2243,8 +2289,8 @@ __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t ro
         n = len < 0 ? 0u : (u32)len < n ? (u32)len : n;
     }
     const u32 k = kout < n ? kout : n;
-    const IdxOut out = IdxOut{p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
-    VT* const ov = p.retval ? (VT*)((uint8_t*)p.out_val + (u64)row * kout * EB) : nullptr;
+    const IdxOut out = IdxOut{(gptr<void>)p.out_idx, p.flags & kFlagIdx64}.at((u64)row * kout);
+    const gptr<VT> ov = p.retval ? (gptr<VT>)((gptr<uint8_t>)p.out_val + (u64)row * kout * EB) : nullptr;
     for (u32 j = k + l; j < kout; j += kWave) {  // -inf columns past a short row (see write_tail)
         out.put(j, j);
         if (ov) ov[j] = EB == 2 ? (VT)0xFF80u : (VT)0xFF800000u;
