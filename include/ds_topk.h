@@ -153,6 +153,34 @@ int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t r
                   int32_t* status_dev, void* stream);
 
 /*
+ * ds_topk_async_noalloc: ds_topk_async for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  It calls no hipMalloc, hipFree or other
+ * allocating routine.
+ *
+ * Arguments, outputs, status and errors are those of ds_topk_async; the
+ * result is the same.  Split rows keep their hand-off state in a static
+ * device array of 16 MiB (DS_TOPK_NOALLOC_SCRATCH_BYTES), one copy per
+ * device, held until the process ends, instead of a workspace; a batch whose
+ * state exceeds it runs as several launches of fewer rows.  A shape of
+ * which one row alone needs more (at most k = 4096 with more than about 190
+ * segments, i.e. rows of several million columns) returns
+ * DS_ERR_UNSUPPORTED before any device call.  The first call on a device
+ * also enqueues one small kernel on `stream` that clears the array's ticket
+ * area.
+ *
+ * Every call on a device shares that device's array, and the array keeps
+ * what the last call left in it: calls that overlap in time on one device
+ * (other streams, other threads, replays of captured graphs running
+ * concurrently with them) race and give wrong results.  Order them, e.g.
+ * on one stream.
+ */
+#define DS_TOPK_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int ds_topk_async_noalloc(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
+                          int32_t k, int sorted_index, int return_value, int32_t* out_idx, void* out_val,
+                          int32_t* status_dev, void* stream);
+
+/*
  * ds_topk_lengths: ds_topk with a valid length per row, in place of -inf
  * tails (a decode-time indexer row covers a context of its own length; the
  * aiutil card, 关键技术亮点 item 1, gives the indexer's vocab range as

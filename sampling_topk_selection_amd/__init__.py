@@ -39,10 +39,11 @@ DS_ORDER_INDEX = 1
 DS_ORDER_VALUE = 2
 
 MAX_K = 4096
+DS_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20  # the no-alloc entry point's static device array
 
-EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_lengths", "ds_topk_ex", "ds_topk_sample", "ds_topk_status_string",
-           "ds_topk_last_error", "ds_topk_plan_for", "ds_topk_set_overrides", "ds_topk_release_stream",
-           "ds_topk_version")
+EXPORTS = ("ds_topk", "ds_topk_async", "ds_topk_async_noalloc", "ds_topk_lengths", "ds_topk_ex", "ds_topk_sample",
+           "ds_topk_status_string", "ds_topk_last_error", "ds_topk_plan_for", "ds_topk_set_overrides",
+           "ds_topk_release_stream", "ds_topk_version")
 
 
 class TopkError(RuntimeError):
@@ -80,6 +81,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ds_topk.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp]
     lib.ds_topk_async.restype = ci
     lib.ds_topk_async.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp, vp]
+    lib.ds_topk_async_noalloc.restype = ci
+    lib.ds_topk_async_noalloc.argtypes = [vp, ci, i64, i64, i64, i32, ci, ci, vp, vp, vp, vp]
     lib.ds_topk_lengths.restype = ci
     lib.ds_topk_lengths.argtypes = [vp, ci, i64, i64, i64, i32, vp, ci, ci, vp, vp, vp]
     lib.ds_topk_sample.restype = ci
@@ -137,6 +140,13 @@ def ds_topk_async(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, 
                   stream: Optional[int]) -> int:
     return load_library().ds_topk_async(in_ptr, dtype, batch, n, row_stride, k, sorted_index, return_value,
                                         out_idx_ptr, out_val_ptr, status_dev_ptr, stream)
+
+
+def ds_topk_async_noalloc(in_ptr: int, dtype: int, batch: int, n: int, row_stride: int, k: int, sorted_index: int,
+                          return_value: int, out_idx_ptr: int, out_val_ptr: Optional[int], status_dev_ptr: int,
+                          stream: Optional[int]) -> int:
+    return load_library().ds_topk_async_noalloc(in_ptr, dtype, batch, n, row_stride, k, sorted_index, return_value,
+                                                out_idx_ptr, out_val_ptr, status_dev_ptr, stream)
 
 
 def ds_topk_status_string(status: int) -> str:

@@ -161,15 +161,21 @@ bool use_small(int64_t n, int32_t k, int sorted_index) {
 // never freed while the process runs (queued work, or a graph captured on
 // the stream, may still use it); growth allocates a larger block, clears it
 // with an ordered memset on the stream and retires the old one.
+// Where the split-row kernels keep their hand-off state: per-row tickets
+// (zero between calls), per-segment metadata and directories, lists.
+struct WsPtrs {
+    uint32_t* ticket = nullptr;
+    uint64_t* meta = nullptr;
+    uint32_t* dir = nullptr;
+    uint64_t* cand = nullptr;
+};
+
 struct Workspace {
     std::mutex mu;
     int device = -1;
     uint8_t* base = nullptr;
     int64_t rows = 0, slots = 0, cands = 0;
-    uint32_t* ticket = nullptr;
-    uint64_t* meta = nullptr;
-    uint32_t* dir = nullptr;
-    uint64_t* cand = nullptr;
+    WsPtrs ptrs;
     std::vector<uint8_t*> retired;
     int32_t* host_word = nullptr;      // pinned: NaN status of synchronous calls
     int32_t* host_word_dev = nullptr;  // its device address
@@ -238,13 +244,13 @@ int ensure(Workspace* ws, int64_t rows, int segs, int32_t per, hipStream_t strea
     }
     if (ws->base) ws->retired.push_back(ws->base);
     uint8_t* p = nb;
-    ws->ticket = (uint32_t*)p;
+    ws->ptrs.ticket = (uint32_t*)p;
     p += al256(rows2 * 4);
-    ws->meta = (uint64_t*)p;
+    ws->ptrs.meta = (uint64_t*)p;
     p += al256(slots2 * 32);
-    ws->dir = (uint32_t*)p;
+    ws->ptrs.dir = (uint32_t*)p;
     p += al256(slots2 * 4 * dstk::kBins);
-    ws->cand = (uint64_t*)p;
+    ws->ptrs.cand = (uint64_t*)p;
     ws->base = nb;
     ws->rows = rows2;
     ws->slots = slots2;
@@ -284,11 +290,9 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
 // Checks the arguments and enqueues the selection on `stream`; a NaN makes
 // the kernels store flag_value into *flag.
 int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
-            int return_value, void* out_idx, void* out_val, Workspace* ws, int32_t* flag, int32_t flag_value,
+            int return_value, void* out_idx, void* out_val, const WsPtrs& ws, int32_t* flag, int32_t flag_value,
             hipStream_t stream, const int32_t* lengths, int index_bytes, const Plan& pl) {
     const bool small = use_small(n, k, sorted_index);
-    int st = ensure(ws, pl.rows_per_launch, small ? 1 : pl.segs, pl.pub_cap, stream);
-    if (st) return st;
     const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
     for (int64_t r0 = 0; r0 < batch; r0 += pl.rows_per_launch) {
         const int64_t rows = batch - r0 < pl.rows_per_launch ? batch - r0 : pl.rows_per_launch;
@@ -305,10 +309,10 @@ int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_str
         prm.retval = return_value ? 1 : 0;
         prm.out_idx = (uint8_t*)out_idx + r0 * k * index_bytes;
         prm.out_val = return_value ? (void*)((uint8_t*)out_val + r0 * k * es) : nullptr;
-        prm.ws_cand = ws->cand;
-        prm.ws_meta = ws->meta;
-        prm.ws_dir = ws->dir;
-        prm.ws_ticket = ws->ticket;
+        prm.ws_cand = ws.cand;
+        prm.ws_meta = ws.meta;
+        prm.ws_dir = ws.dir;
+        prm.ws_ticket = ws.ticket;
         prm.pub_cap = pl.pub_cap;
         prm.flag = flag;
         prm.flag_value = flag_value;
@@ -375,7 +379,7 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     Workspace* ws = workspace_for(dev, stream);
     std::lock_guard<std::mutex> g(ws->mu);
-    st = ensure_host_word(ws);
+    st = ensure(ws, pl.rows_per_launch, use_small(n, k, sorted_index) ? 1 : pl.segs, pl.pub_cap, stream);
     if (st) return st;
     int32_t* flag = status_dev;
     int32_t flag_value = DS_ERR_NAN;
@@ -383,8 +387,8 @@ int run(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride,
         flag = ws->host_word_dev;
         flag_value = next_epoch(ws);
     }
-    st = enqueue(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, ws, flag, flag_value,
-                 stream, lengths, index_bytes, pl);
+    st = enqueue(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, ws->ptrs, flag,
+                 flag_value, stream, lengths, index_bytes, pl);
     if (st || status_dev) return st;
     e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -446,11 +450,11 @@ int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stri
     make_plan(dtype, batch, n, k, &pl);
     Workspace* ws = workspace_for(dev, stream);
     std::lock_guard<std::mutex> g2(ws->mu);
-    st = ensure_host_word(ws);
+    st = ensure(ws, pl.rows_per_launch, use_small(n, k, DS_ORDER_VALUE) ? 1 : pl.segs, pl.pub_cap, stream);
     if (st) return st;
     const int32_t flag_value = next_epoch(ws);
-    st = enqueue(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, ws, ws->host_word_dev, flag_value,
-                 stream, nullptr, 4, pl);
+    st = enqueue(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, ws->ptrs, ws->host_word_dev,
+                 flag_value, stream, nullptr, 4, pl);
     if (st) return st;
     if (dtype == DS_DTYPE_BF16)
         hipLaunchKernelGGL(dssample::sample_rows<uint16_t>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
@@ -518,6 +522,108 @@ int release(hipStream_t stream) {
 
 }  // namespace
 
+// ------------------------------------------------------------------ no-alloc
+// ds_topk_async_noalloc keeps the split-row hand-off state (tickets,
+// metadata, directories, lists) in this array instead of a workspace.  Each
+// device the library runs on holds its own copy until the process ends.
+// Host code never passes this name to a kernel or a copy (on the host it is
+// only a stand-in): it uses the copy's device address from
+// hipGetSymbolAddress, taken once per device.
+constexpr int64_t kScratchBytes = DS_TOPK_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t kScratchTicketBytes = 4096;  // tickets of up to 1024 rows, always at offset 0
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+static_assert(kMaxSplitSlots / 2 * 4 <= kScratchTicketBytes, "the ticket area holds the rows of any split launch");
+
+__global__ void clear_words(uint32_t* p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices] = {};
+
+// The device address of the current device's scratch copy.  The first use
+// on a device takes the address and clears the ticket area with a kernel on
+// `stream` (the array starts zeroed and every completed call leaves its
+// tickets at zero; the clear makes that independent of what ran before).
+int scratch_for(hipStream_t stream, uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DS_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(DS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        const int words = (int)(kScratchTicketBytes / 4);
+        hipLaunchKernelGGL(clear_words, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, stream, (uint32_t*)ptr,
+                           words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch ticket clear");
+        g_scratch[dev] = (uint8_t*)ptr;
+    }
+    *out = g_scratch[dev];
+    return DS_OK;
+}
+
+// Bytes after the ticket area that `rows` split rows of the plan use.
+int64_t scratch_state_bytes(const Plan& pl, int64_t rows) {
+    const int64_t slots = rows * pl.segs;
+    return al256(slots * 32) + al256(slots * 4 * dstk::kBins) + al256(slots * (int64_t)pl.pub_cap * 8);
+}
+
+// Rows per launch whose hand-off state fits the scratch (the plan's own, or
+// fewer); an error if one row alone does not fit.
+int scratch_rows(const Plan& pl, int64_t* rows_out) {
+    const int64_t room = kScratchBytes - kScratchTicketBytes;
+    const int64_t one = scratch_state_bytes(pl, 1);
+    if (one > room)
+        return fail(DS_ERR_UNSUPPORTED,
+                    "ds_topk_async_noalloc: one row of %d segments publishing up to %d entries needs %lld bytes of "
+                    "hand-off state; its static scratch holds %lld (use ds_topk_async)",
+                    pl.segs, pl.pub_cap, (long long)one, (long long)room);
+    int64_t rows = room / one < pl.rows_per_launch ? room / one : pl.rows_per_launch;
+    while (rows > 1 && scratch_state_bytes(pl, rows) > room) --rows;
+    *rows_out = rows;
+    return DS_OK;
+}
+
+int run_noalloc(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
+                int return_value, void* out_idx, void* out_val, int32_t* status_dev, hipStream_t stream) {
+    g_err.clear();
+    if (!status_dev) return fail(DS_ERR_INVALID_ARGUMENT, "status_dev is NULL");
+    int st = check_args(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, 4);
+    if (st) return st;
+    if (batch == 0) return DS_OK;
+    Plan pl;
+    make_plan(dtype, batch, n, k, &pl);
+    WsPtrs ws;
+    if (!use_small(n, k, sorted_index) && pl.segs > 1) {
+        int64_t rows = 0;
+        st = scratch_rows(pl, &rows);  // (checked before any device call)
+        if (st) return st;
+        pl.rows_per_launch = rows;
+        uint8_t* base = nullptr;
+        st = scratch_for(stream, &base);
+        if (st) return st;
+        const int64_t slots = rows * pl.segs;
+        ws.ticket = (uint32_t*)base;
+        ws.meta = (uint64_t*)(base + kScratchTicketBytes);
+        ws.dir = (uint32_t*)((uint8_t*)ws.meta + al256(slots * 32));
+        ws.cand = (uint64_t*)((uint8_t*)ws.dir + al256(slots * 4 * dstk::kBins));
+    }
+    return enqueue(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, ws, status_dev,
+                   DS_ERR_NAN, stream, nullptr, 4, pl);
+}
+
+}  // namespace
+
 extern "C" {
 
 int ds_topk(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
@@ -532,6 +638,12 @@ int ds_topk_async(const void* in, int dtype, int64_t batch, int64_t n, int64_t r
     if (!status_dev) return fail(DS_ERR_INVALID_ARGUMENT, "status_dev is NULL");
     return run(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, status_dev,
                (hipStream_t)stream);
+}
+int ds_topk_async_noalloc(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
+                          int sorted_index, int return_value, int32_t* out_idx, void* out_val, int32_t* status_dev,
+                          void* stream) {
+    return run_noalloc(in, dtype, batch, n, row_stride, k, sorted_index, return_value, out_idx, out_val, status_dev,
+                       (hipStream_t)stream);
 }
 int ds_topk_lengths(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
                     const int32_t* lengths, int sorted_index, int return_value, int32_t* out_idx, void* out_val,

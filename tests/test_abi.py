@@ -102,6 +102,24 @@ def test_pointer_errors(pkg):
         assert pkg.ds_topk_plan_for(BF, 4, 64, 64, 8, order)[0] == 0
 
 
+def test_noalloc_host_checks(pkg):
+    """The no-alloc entry point checks its arguments like ds_topk_async, and
+    rejects a row whose split-row state exceeds its static array, all before
+    any HIP call."""
+    na = pkg.ds_topk_async_noalloc
+    assert na(FAKE, BF, 4, 64, 64, 8, 0, 0, FAKE, None, None, None) == 1  # no status word
+    assert na(None, BF, 4, 64, 64, 8, 0, 0, FAKE, None, FAKE, None) == 1
+    assert na(FAKE, BF, 4, 64, 64, 65, 0, 0, FAKE, None, FAKE, None) == 1  # k > n
+    assert na(FAKE + 2, BF, 4, 64, 64, 8, 0, 0, FAKE, None, FAKE, None) == 3
+    assert na(FAKE, BF, 0, 64, 64, 8, 0, 0, FAKE, None, FAKE, None) == 0  # no rows
+    n, k = 1 << 23, 4096  # 256 segments publishing 9216 entries each: about 21 MB for one row
+    st, p = pkg.ds_topk_plan_for(BF, 1, n, n, k)
+    assert st == 0 and p.segments == 256
+    assert p.segments * (32 + 4 * 2048 + 8 * p.publish_capacity) > pkg.DS_TOPK_NOALLOC_SCRATCH_BYTES
+    assert na(FAKE, BF, 1, n, n, k, 0, 0, FAKE, None, FAKE, None) == 2
+    assert "static scratch" in pkg.ds_topk_last_error()
+
+
 def test_k_limits_from_pages(pkg):
     import json
 
