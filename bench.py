@@ -43,26 +43,54 @@ METRIC = "effective HBM GB/s (% peak), bf16 4×204800 k=1024 & fp32 64×129280 k
 PEAK_GBS = 8000.0  # MI355X HBM3E
 STEP_WORKLOADS = ("C2", "C3")
 DOMINANT = "C3"
-TRAFFIC_FILES = {"C3": "topk_rows_fp32_sampler_64x129280_k512_traffic.txt"}
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES[workload])
+TRAFFIC_FILES = {"C2": "topk_rows_bf16_indexer_4x204800_k1024_traffic.txt",
+                 "C3": "topk_rows_fp32_sampler_64x129280_k512_traffic.txt"}
+STATS_FILE = "topk_rows_bench_step_indexer_bf16_4x204800_sampler_fp32_64x129280_kernel_stats.txt"
+KERNEL_NAMES = {"C2": "topk_rows<2, 512, 2, 8192>", "C3": "topk_rows<4, 512, 4, 8192>"}
+
+
+def _current(path: str):
+    """The lines of a committed profile summary, if it was taken on the
+    current kernel sources; else None."""
     if not os.path.exists(path):
         return None
+    from sampling_topk_selection_amd.build import kernel_source_sha
+
+    lines = open(path).read().splitlines()
+    if not any(l.replace("#", "").strip() == "kernel_source_sha: %s" % kernel_source_sha() for l in lines):
+        return None
+    return lines
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch (fetch, write, total) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel
+    sources; else None."""
+    lines = _current(os.path.join(ROOT, "profiles", TRAFFIC_FILES[workload]))
+    if lines is None:
+        return None
     kv = {}
-    for line in open(path):
+    for line in lines:
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    from sampling_topk_selection_amd.build import kernel_source_sha
-
-    if kv.get("kernel_source_sha") != kernel_source_sha():
-        return None
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
+        return {k: int(float(kv[k + "_bytes_per_launch"])) for k in ("fetch", "write", "hbm")}
     except (KeyError, ValueError):
         return None
+
+
+def load_profiled_avg_us(workload: str):
+    """The kernel's average duration in the committed rocprofv3 kernel
+    statistics of the bench command, if taken on the current sources."""
+    lines = _current(os.path.join(ROOT, "profiles", STATS_FILE))
+    if lines is None:
+        return None
+    for line in lines:
+        if KERNEL_NAMES[workload] in line:
+            # name, calls, avg_us, min_us, max_us, time%
+            return float(line.split(")")[-1].split()[1])
+    return None
 
 
 def parse_args():
@@ -102,7 +130,7 @@ def main() -> int:
 
     pkg.load_library()
     calib = ctypes.CDLL(builder.CALIB_LIB)
-    calib.calib_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    calib.calib_empty.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
     calib.calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                  ctypes.c_void_p]
     calib.calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
@@ -170,69 +198,110 @@ def main() -> int:
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
     per = {}
-    if not args.no_extras:
+
+    def per_call_ms(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(ts) / len(ts), ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+
+    reps = max(20, args.steps)
+    for cfg in STEP_WORKLOADS:
+        # ------------------------------------------------------------ calibration (also in profiler runs)
+        d = W[cfg]
+        w = d["w"]
+        grid = d["plan"].grid
+        out_buf = torch.empty(max(1, grid), dtype=torch.int32, device=dev)
+        nbytes_in = w.batch * w.row_stride * w.elem_size
+
+        def rd(i, c=cfg, g=grid, ob=out_buf, nb=nbytes_in):
+            X = W[c]["X"]
+            calib.calib_read(X[i % W[c]["copies"]].data_ptr(), nb, g, ob.data_ptr(), sptr)
+
+        ravg, rmed, _, _ = per_call_ms(rd, reps)
+        # launch floor: empty kernels of the same grid, back to back
+        calib.calib_empty(grid, 20, sptr)
+        fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fa.record(stream)
+        calib.calib_empty(grid, 200, sptr)
+        fb.record(stream)
+        torch.cuda.synchronize()
+        empty_us = fa.elapsed_time(fb) * 1e3 / 200
+        per[cfg] = {
+            "shape": "%s %dx%d k=%d sorted=%d values=%d" % (w.dtype, w.batch, w.n, w.k, w.sorted_index,
+                                                            w.return_value),
+            "algorithmic_bytes": d["bytes"],
+            "segments_per_row": d["plan"].segments,
+            "workgroups": grid,
+            "input_copies": d["copies"],
+            "calib_stream_read_us": round(ravg * 1e3, 3),
+            "calib_stream_read_GBps": round(nbytes_in / (ravg * 1e-3) / 1e9, 1),
+            "calib_empty_kernel_us": round(empty_us, 3),
+            "hbm_traffic_bytes_per_launch": load_traffic(cfg),
+        }
+        if args.no_extras:
+            continue
         # ------------------------------------------------------------ per-call kernel time
-        def per_call_ms(fn, reps):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            for i, (a, b) in enumerate(evs):
-                a.record(stream)
-                fn(i)
-                b.record(stream)
-            torch.cuda.synchronize()
-            ts = sorted(a.elapsed_time(b) for a, b in evs)
-            return sum(ts) / len(ts), ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
+        avg, med, p10, p90 = per_call_ms(lambda i, c=cfg: call(c, i), reps)
+        wavg, wmed, _, _ = per_call_ms(lambda i, c=cfg: call(c, 0), reps)
+        per[cfg].update({
+            "us_per_call_mean": round(avg * 1e3, 3),
+            "us_per_call_median": round(med * 1e3, 3),
+            "us_p10": round(p10 * 1e3, 3),
+            "us_p90": round(p90 * 1e3, 3),
+            "GBps": round(d["bytes"] / (avg * 1e-3) / 1e9, 1),
+            "pct_peak": round(100.0 * d["bytes"] / (avg * 1e-3) / 1e9 / PEAK_GBS, 2),
+            "rows_per_s": round(w.batch / (avg * 1e-3), 1),
+            "warm_us_per_call": round(wavg * 1e3, 3),
+            "warm_GBps": round(d["bytes"] / (wavg * 1e-3) / 1e9, 1),
+            "pct_of_stream_read": round(100.0 * ravg / avg, 1),
+        })
 
-        reps = max(20, args.steps)
-        for cfg in STEP_WORKLOADS:
-            d = W[cfg]
-            w = d["w"]
-            avg, med, p10, p90 = per_call_ms(lambda i, c=cfg: call(c, i), reps)
-            wavg, wmed, _, _ = per_call_ms(lambda i, c=cfg: call(c, 0), reps)
-            grid = d["plan"].grid
-            out_buf = torch.empty(max(1, grid), dtype=torch.int32, device=dev)
-            nbytes_in = w.batch * w.row_stride * w.elem_size
-
-            def rd(i, c=cfg, g=grid, ob=out_buf, nb=nbytes_in):
-                X = W[c]["X"]
-                calib.calib_read(X[i % W[c]["copies"]].data_ptr(), nb, g, ob.data_ptr(), sptr)
-
-            ravg, rmed, _, _ = per_call_ms(rd, reps)
-            eavg, emed, _, _ = per_call_ms(lambda i, g=grid: calib.calib_empty(g, sptr), reps)
-            per[cfg] = {
-                "shape": "%s %dx%d k=%d sorted=%d values=%d" % (w.dtype, w.batch, w.n, w.k, w.sorted_index,
-                                                                w.return_value),
-                "algorithmic_bytes": d["bytes"],
-                "segments_per_row": d["plan"].segments,
-                "workgroups": grid,
-                "input_copies": d["copies"],
-                "us_per_call_mean": round(avg * 1e3, 3),
-                "us_per_call_median": round(med * 1e3, 3),
-                "us_p10": round(p10 * 1e3, 3),
-                "us_p90": round(p90 * 1e3, 3),
-                "GBps": round(d["bytes"] / (avg * 1e-3) / 1e9, 1),
-                "pct_peak": round(100.0 * d["bytes"] / (avg * 1e-3) / 1e9 / PEAK_GBS, 2),
-                "rows_per_s": round(w.batch / (avg * 1e-3), 1),
-                "warm_us_per_call": round(wavg * 1e3, 3),
-                "warm_GBps": round(d["bytes"] / (wavg * 1e-3) / 1e9, 1),
-                "calib_stream_read_us": round(ravg * 1e3, 3),
-                "calib_stream_read_GBps": round(nbytes_in / (ravg * 1e-3) / 1e9, 1),
-                "pct_of_stream_read": round(100.0 * ravg / avg, 1),
-                "calib_empty_kernel_us": round(eavg * 1e3, 3),
-            }
-
-        # synchronous entry point: kernel + status readback per call
+    if not args.no_extras:
+        # synchronous entry point (kernel + stream wait + status check) per
+        # call: through the C ABI on preallocated outputs, and through the
+        # Python topk(), which also allocates its outputs
         for cfg in STEP_WORKLOADS:
             d = W[cfg]
             w = d["w"]
             x = d["x0"]
+
+            def sync_call(c=cfg, xx=x):
+                dd = W[c]
+                ww = dd["w"]
+                rc = pkg.ds_topk(xx.data_ptr(), dd["dt"], ww.batch, ww.n, ww.row_stride, ww.k,
+                                 int(ww.sorted_index), int(ww.return_value), dd["idx"].data_ptr(),
+                                 dd["val"].data_ptr() if dd["val"] is not None else None, sptr)
+                if rc != 0:
+                    raise RuntimeError("ds_topk failed: %s" % pkg.ds_topk_last_error())
+
+            r = 50
+            for _ in range(3):
+                sync_call()
+            t = time.perf_counter()
+            for _ in range(r):
+                sync_call()
+            per[cfg]["sync_call_us"] = round((time.perf_counter() - t) / r * 1e6, 1)
             for _ in range(3):
                 pkg.topk(x, w.k, sorted_index=w.sorted_index, return_value=w.return_value)
-            r = 50
             t = time.perf_counter()
             for _ in range(r):
                 pkg.topk(x, w.k, sorted_index=w.sorted_index, return_value=w.return_value)
-            per[cfg]["sync_call_us"] = round((time.perf_counter() - t) / r * 1e6, 1)
+            per[cfg]["sync_call_python_us"] = round((time.perf_counter() - t) / r * 1e6, 1)
+            # the same kernels enqueued back to back on one (warm) input: the
+            # kernel time the synchronous call adds its wait to
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(r):
+                call(cfg, 0)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            per[cfg]["warm_back_to_back_us"] = round(a_.elapsed_time(b_) * 1e3 / r, 3)
 
     modes = {}
     if not args.no_extras:
@@ -261,6 +330,10 @@ def main() -> int:
         modes["C4_neg_inf_tails_us"] = round(mode_us(x4, w4, return_value=True), 3)
         modes["C4_lengths_us"] = round(mode_us(x4, w4, return_value=True, lengths=l4), 3)
         modes["C4_valid_bytes"] = int(sum(w4.meta["lengths"]) * 2 + w4.batch * w4.k * 6)
+        # heavy ties at the largest k: 16 levels ascending along each row
+        w5 = make_workload("C5")
+        x5 = torch.from_numpy(np.ascontiguousarray(w5.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+        modes["C5_max_k_us"] = round(mode_us(x5, w5, return_value=True, sorted_index=True), 3)
         # many short rows: one wave per row
         for (bsz, nn, kk) in ((4096, 256, 64), (16384, 128, 16)):
             gs = torch.Generator(device="cpu").manual_seed(bsz + nn)
@@ -313,7 +386,9 @@ def main() -> int:
     from sampling_topk_selection_amd.build import kernel_source_sha
 
     achieved = W[DOMINANT]["bytes"] / (dom_us * 1e-6) / 1e9
-    traffic = load_traffic(DOMINANT)
+    tr = load_traffic(DOMINANT)
+    traffic = tr["hbm"] if tr else None
+    prof_us = load_profiled_avg_us(DOMINANT)
     roofline = {
         "bound": "hbm",
         "kernel": "topk_rows<4, 512, %d, %d> (fp32 sampler shape: 64 x 129280, k=512)" % (
@@ -326,6 +401,11 @@ def main() -> int:
         "algorithmic_bytes_per_launch": W[DOMINANT]["bytes"],
         "avg_launch_us": round(dom_us, 3),
         "launches_timed": dom_reps,
+        # the same ratio with the committed rocprofv3 average of this kernel
+        # (profiles/, kernel statistics of the bench command), when taken on
+        # the current sources
+        "profiled_avg_us": prof_us,
+        "frac_profiled": round(W[DOMINANT]["bytes"] / (prof_us * 1e-6) / 1e9 / PEAK_GBS, 4) if prof_us else None,
         "kernel_source_sha": kernel_source_sha(),
     }
 

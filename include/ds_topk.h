@@ -122,9 +122,12 @@ enum ds_topk_status {
  * ds_topk_release_stream, so work already queued, or a graph captured
  * earlier, never sees freed memory.  Growth never synchronises.
  *
- * Synchronisation: the call enqueues the kernel(s) on `stream`, waits for
- * the stream, then reads the NaN status from the pinned host word the
- * kernels store it into; when it returns, the outputs are complete.
+ * Synchronisation: the call enqueues the kernel(s) on `stream`, then one
+ * single-thread kernel that stores the call's completion tag and NaN status
+ * into a pinned host word, and spins on that word (up to 2 ms, then it
+ * waits for the stream, which also reports a failed kernel); when it
+ * returns, the outputs are complete.  A synchronous call on a capturing
+ * stream returns DS_ERR_HIP before enqueuing anything.
  * Argument errors are returned before any HIP call, and nothing is
  * written.  Calls on different streams may run concurrently; they use
  * different workspaces.  Calls on one stream share its workspace, so they

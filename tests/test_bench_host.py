@@ -11,6 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import pytest  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -29,8 +30,12 @@ def _summary(path):
     return kv
 
 
-def test_traffic_summary_is_consistent():
-    path = os.path.join(ROOT, "profiles", bench.TRAFFIC_FILES["C3"])
+MIN_READ = {"C2": 4 * 204800 * 2, "C3": 64 * 129280 * 4}
+
+
+@pytest.mark.parametrize("cfg", ["C2", "C3"])
+def test_traffic_summary_is_consistent(cfg):
+    path = os.path.join(ROOT, "profiles", bench.TRAFFIC_FILES[cfg])
     kv = _summary(path)
     fetch, write = int(kv["fetch_bytes_per_launch"]), int(kv["write_bytes_per_launch"])
     assert fetch + write == int(kv["hbm_bytes_per_launch"])
@@ -39,7 +44,8 @@ def test_traffic_summary_is_consistent():
     assert abs(float(kv["fetch_scale"]) * float(kv["copy_FETCH_SIZE_KiB"]) * 1024 - copy) < 0.01 * copy
     assert abs(float(kv["write_scale"]) * float(kv["copy_WRITE_SIZE_KiB"]) * 1024 - copy) < 0.01 * copy
     # at least the algorithmic input bytes are read
-    assert fetch >= 64 * 129280 * 4
+    assert fetch >= MIN_READ[cfg]
+    assert bench.KERNEL_NAMES[cfg] in kv["kernel"]
 
 
 def test_traffic_used_only_for_the_current_sources(tmp_path, monkeypatch):
@@ -52,9 +58,28 @@ def test_traffic_used_only_for_the_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     current = _summary(src).get("kernel_source_sha") == kernel_source_sha()
     got = bench.load_traffic("C3")
-    assert (got == int(_summary(src)["hbm_bytes_per_launch"])) if current else got is None
+    assert (got["hbm"] == int(_summary(src)["hbm_bytes_per_launch"])) if current else got is None
     text = open(dst).read().replace("kernel_source_sha: ", "kernel_source_sha: x")
     open(dst, "w").write(text)
     assert bench.load_traffic("C3") is None
     os.remove(dst)
     assert bench.load_traffic("C3") is None
+
+
+def test_profiled_average_read_from_the_kernel_statistics(tmp_path, monkeypatch):
+    from sampling_topk_selection_amd.build import kernel_source_sha
+
+    os.makedirs(tmp_path / "profiles")
+    dst = tmp_path / "profiles" / bench.STATS_FILE
+    rows = ["# rocprofv3 kernel statistics", "# command: x", "# kernel_source_sha: %s" % kernel_source_sha(), "",
+            "%-70s %7s %11s %11s %11s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "time%"),
+            "%-70s %7d %11.3f %11.3f %11.3f %7.2f" % ("void dstk::topk_rows<4, 512, 4, 8192>(dstk::Params)", 48,
+                                                      21.5, 20.0, 30.0, 55.0),
+            "%-70s %7d %11.3f %11.3f %11.3f %7.2f" % ("void dstk::topk_rows<2, 512, 2, 8192>(dstk::Params)", 25,
+                                                      12.25, 11.0, 14.0, 20.0)]
+    open(dst, "w").write("\n".join(rows) + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_profiled_avg_us("C3") == 21.5
+    assert bench.load_profiled_avg_us("C2") == 12.25
+    open(dst, "w").write("\n".join(rows).replace("kernel_source_sha: ", "kernel_source_sha: x") + "\n")
+    assert bench.load_profiled_avg_us("C3") is None
