@@ -69,8 +69,8 @@ def traffic(fetch_csv: str, write_csv: str, out_txt: str, kernel_sub: str, copy_
     cf, cw = _pick(fm, COPY_KERNEL), _pick(wm, COPY_KERNEL)
     fetch_scale = copy_bytes / (fm[cf] * 1024.0)
     write_scale = copy_bytes / (wm[cw] * 1024.0)
-    fetch_b = fm[kf] * 1024.0 * fetch_scale
-    write_b = wm[kw] * 1024.0 * write_scale
+    fetch_b = round(fm[kf] * 1024.0 * fetch_scale)
+    write_b = round(wm[kw] * 1024.0 * write_scale)
     lines = [
         "# HBM traffic per launch from rocprofv3 counters, scaled by a copy of known size",
         "# commands: %s" % commands,
@@ -85,9 +85,9 @@ def traffic(fetch_csv: str, write_csv: str, out_txt: str, kernel_sub: str, copy_
         "copy_WRITE_SIZE_KiB: %.1f" % wm[cw],
         "fetch_scale: %.4f" % fetch_scale,
         "write_scale: %.4f" % write_scale,
-        "fetch_bytes_per_launch: %.0f" % fetch_b,
-        "write_bytes_per_launch: %.0f" % write_b,
-        "hbm_bytes_per_launch: %.0f" % (fetch_b + write_b),
+        "fetch_bytes_per_launch: %d" % fetch_b,
+        "write_bytes_per_launch: %d" % write_b,
+        "hbm_bytes_per_launch: %d" % (fetch_b + write_b),
     ]
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
