@@ -114,22 +114,25 @@ __device__ __forceinline__ u32 comp_col(u64 c) {
 template <class E>
 struct PreFilter;
 
+// Next value above the finite nonzero value of bits b (sign-magnitude, one
+// step in the last place, toward +inf).
+__device__ __forceinline__ u32 next_up(u32 b, u32 sign) { return (b & sign) ? b - 1u : b + 1u; }
+
 template <>
 struct PreFilter<Elem<2>> {
-    float t_lo;  // for the low half of a dword: exact bf16 value << 16
-    float t_hi;  // for the high half read as a whole dword (low half is noise):
-                 // the least float whose upper 16 bits are the threshold's
+    float t;   // the threshold value, exact (bf16 << 16)
+    float ts;  // the next bf16 value above it: "!(x < ts)" is "x > t" (strict_ok)
+    bool strict_ok;  // t is finite or -inf, and not a zero
     __device__ void set(u64 L) {
-        u32 b = Elem<2>::bits(comp_key<Elem<2>>(L));
-        t_lo = __uint_as_float(b << 16);
-        t_hi = __uint_as_float((b << 16) | ((b & 0x8000u) ? 0xFFFFu : 0u));
+        const u32 b = Elem<2>::bits(comp_key<Elem<2>>(L));
+        t = __uint_as_float(b << 16);
+        strict_ok = (b & 0x7FFFu) != 0u && b != 0x7F80u;
+        ts = __uint_as_float(next_up(b, 0x8000u) << 16);
     }
+    // Each half is compared alone (the other zeroed): read with its
+    // neighbour, a -inf half would look like a NaN and always pass.
     __device__ u32 any(u32 d) const {
-        return (u32)!(__uint_as_float(d) < t_hi) | (u32)!(__uint_as_float(d << 16) < t_lo);
-    }
-    // bit 0: the low half may pass, bit 1: the high half may pass
-    __device__ u32 pass2(u32 d) const {
-        return (u32)!(__uint_as_float(d << 16) < t_lo) | ((u32)!(__uint_as_float(d) < t_hi) << 1);
+        return (u32)!(__uint_as_float(d & 0xFFFF0000u) < t) | (u32)!(__uint_as_float(d << 16) < t);
     }
 };
 
@@ -158,7 +161,7 @@ __device__ __forceinline__ bool pass_slot(const PreFilter<Elem<4>>& pf, const u3
 }
 template <int s>
 __device__ __forceinline__ bool pass_slot(const PreFilter<Elem<2>>& pf, const u32 (&dw)[4]) {
-    return (s & 1) ? !(__uint_as_float(dw[s >> 1]) < pf.t_hi) : !(__uint_as_float(dw[s >> 1] << 16) < pf.t_lo);
+    return (s & 1) ? !(__uint_as_float(dw[s >> 1] & 0xFFFF0000u) < pf.t) : !(__uint_as_float(dw[s >> 1] << 16) < pf.t);
 }
 // Is element s a NaN?  (Its value widened to fp32: a NaN stays a NaN.)
 template <int s>
@@ -223,6 +226,9 @@ struct Smem {
     u32 outcount;        // emit: output slots handed out
     u32 pflag[2];        // scan: "some wave has a tile left over", two slots
     u32 wfill[16];       // scan: raw entries each wave has appended since the last sync
+    u32 tie_min, tie_max;  // seed: least and greatest key in the crowded bin
+    u32 tie_col;           // seed: column of the tied k-th entry
+    u32 tie_cnt[8];        // seed: the crowded bin's entries per bound tile
     u32 lwsum[16];       // block_locate: per-wave bin totals
     u32 lwfirst[16];     // block_locate: per-wave highest non-empty bin (waves with any)
     u64 trash[64];       // scan: written by the lanes that append nothing
@@ -459,6 +465,8 @@ __device__ __forceinline__ u32 block_excl_scan(Smem<CAP>& sm, u32 v, u32* total)
 }
 
 constexpr int kBatch = 8;  // LDS loads kept in flight per thread in buffer passes
+// A seed bin this crowded is checked for a single value (the tied seed bound).
+constexpr u32 kTiedBin = 512;
 
 // MIN and MAX over the entries of buf[lo, hi) whose bits under `mask` equal
 // `prefix` (MIN = ~0, MAX = 0 when none do).  Also zeroes the histogram for
@@ -1531,11 +1539,23 @@ __device__ __forceinline__ bool append_tile(Smem<CAP>& sm, const ScanCtx& cx, Sc
     constexpr int kTileVecs = WG;
     const u32 dw[4] = {x[0], x[1], x[2], x[3]};
     const u32 vi = (u32)(vb + (int)threadIdx.x);
+    // With an exact bound, a tile whose columns all lie above the bound's
+    // can only add values strictly above the bound's value (a tie there has
+    // the smaller composite): filter on the next value up, and skip the
+    // composite test.  (Not for a zero or +inf bound value: -0 and +0 are
+    // equal as floats but not here, and nothing lies above +inf.)
+    // (bf16 only, with the tied seed bound; see kTiedSeed)
+    bool strict = false;
+    PreFilter<E> q = pf;
+    if constexpr (E::kKeyBits == 16) {
+        strict = st.exact && pf.strict_ok && (u32)vb * (u32)P > comp_col<E>(st.L);
+        if (strict) q.t = pf.ts;
+    }
     u64 m[P];
     u64 any = 0;
     static_for<P>([&](auto S_) {
         constexpr int s = decltype(S_)::value;
-        m[s] = __ballot(pass_slot<s>(pf, dw));
+        m[s] = __ballot(pass_slot<s>(q, dw));
         any |= m[s];
     });
     if (any == 0) return true;
@@ -1546,7 +1566,7 @@ __device__ __forceinline__ bool append_tile(Smem<CAP>& sm, const ScanCtx& cx, Sc
             m[s] &= __ballot((int)vi < cx.v1 && vi * P + s < cx.n);
         });
     }
-    if (st.exact) {
+    if (st.exact && !strict) {
         static_for<P>([&](auto S_) {
             constexpr int s = decltype(S_)::value;
             if (m[s]) {
@@ -1713,6 +1733,135 @@ struct Slot {
     }
 };
 
+// ------------------------------------------------------------------ crowded seed
+struct SeedBound {
+    u64 L;
+    u32 exact;
+};
+
+// The seed bound when the bin of the seed's k-th entry is crowded: heavy
+// ties (runs of one value such as -inf padding, quantized or monotone rows)
+// look like this.  The seed tiles are read again (from the cache) with the
+// segment's first and last tiles -- the largest values of a monotone row lie
+// at one end, the tied entries with the lowest columns at the first -- and
+// counted together; the end tiles only tighten the bound and are appended
+// in their turn.  If the bin of the k-th counted entry holds one value, its
+// entries differ only in their columns, and the k-th composite is that value
+// at the r-th lowest of those columns (a lower column is a larger
+// composite): that exact bound is returned, with survivors to be tested
+// against it; otherwise the bin's floor.  The histogram is zero on entry and
+// on return.  Out of line, so the common path keeps its registers.
+template <class E, int WG, int CAP, int KS>
+__device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buffer_rsrc_t rsrc, VecBases<KS> sb,
+                                                     int v0, int v1, u32 n, u32 k, u32 ntiles) {
+    using SL = Slot<E, 1, WG>;
+    constexpr int kB = KS + 2;
+    constexpr int kTileVecs = WG;
+    const u32 tid = threadIdx.x;
+    int bvb[kB];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) bvb[i] = sb.b[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int tv = v0 + (j == 0 ? 0 : (int)(ntiles - 1u) * kTileVecs);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) tv = bvb[i] == tv ? v1 : tv;  // already a seed tile
+        if (j == 1 && tv == bvb[KS]) tv = v1;                     // one tile only
+        bvb[KS + j] = tv;
+    }
+    u32x4 bt[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) bt[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(bvb[i] + (int)tid - v0) * 16u, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        const u32x4 xs[1] = {bt[i]};
+#pragma unroll
+        for (int s_ = 0; s_ < SL::kSlots; ++s_) {
+            u32 bits, col;
+            bool valid;
+            SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
+            hist_add(sm.hist, top_digit(compose<E>(E::key(bits), col)), valid);
+        }
+    }
+    __syncthreads();
+    block_locate<WG, CAP>(sm, k, 0u, true);
+    SeedBound r{sm.loc_c[0] > 0 ? digit_floor(sm.loc_digit[0]) : 0ull, 0u};
+    if (sm.loc_c[0] < kTiedBin) return r;
+    // one value in bin b1?  (least and greatest key; the bin's entries per
+    // tile, tc[i] this thread's)
+    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0];
+    u32 kmin = ~0u, kmax = 0u, tc[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        tc[i] = 0;
+        const u32x4 xs[1] = {bt[i]};
+#pragma unroll
+        for (int s_ = 0; s_ < SL::kSlots; ++s_) {
+            u32 bits, col;
+            bool valid;
+            SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
+            const u32 kk = E::key(bits);
+            if (valid && top_digit(compose<E>(kk, col)) == b1) {
+                kmin = kk < kmin ? kk : kmin;
+                kmax = kk > kmax ? kk : kmax;
+                ++tc[i];
+            }
+        }
+    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    u32 wc[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) wc[i] = __builtin_amdgcn_readlane(wave_incl_scan(tc[i]), kWave - 1);
+    if (lane_id() == 0) {
+        atomicMin(&sm.tie_min, kmin);
+        atomicMax(&sm.tie_max, kmax);
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (wc[i]) atomicAdd(&sm.tie_cnt[i], wc[i]);
+    }
+    __syncthreads();
+    const u32 key = sm.tie_min;
+    if (key != sm.tie_max) return r;
+    // the tile holding the r1-th lowest column of the bin: tiles are whole
+    // column ranges, so order them by start
+    u32 mine = 0, rr = 0;
+    int which = -1;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        u32 below = 0;
+#pragma unroll
+        for (int j = 0; j < kB; ++j) below += bvb[j] < bvb[i] ? sm.tie_cnt[j] : 0u;
+        if (below < r1 && r1 <= below + sm.tie_cnt[i]) {
+            mine = tc[i];
+            rr = r1 - below;
+            which = i;
+        }
+    }
+    // inside it, column order is thread order, then slot order
+    u32 tot;
+    const u32 excl = block_excl_scan<WG, CAP>(sm, mine, &tot);
+    if (excl < rr && rr <= excl + mine) {
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            if (i != which) continue;
+            const u32x4 xs[1] = {bt[i]};
+            u32 seen = excl;
+#pragma unroll
+            for (int s_ = 0; s_ < SL::kSlots; ++s_) {
+                u32 bits, col;
+                bool valid;
+                SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
+                if (valid && top_digit(compose<E>(E::key(bits), col)) == b1 && ++seen == rr) sm.tie_col = col;
+            }
+        }
+    }
+    __syncthreads();
+    r.L = compose<E>(key, sm.tie_col);
+    r.exact = 1u;
+    return r;
+}
+
 // Exact selection of the k largest of buf[0, cnt) (bin b1 holds the k-th,
 // rank r1 of c1 inside it) and output, the −inf tail up to kout, then the
 // NaN report; the workgroup ends here.
@@ -1869,6 +2018,10 @@ void topk_rows(Params p) {
         sm.outcount = 0;
         sm.pflag[0] = 0;
         sm.pflag[1] = 0;
+        sm.tie_min = ~0u;
+        sm.tie_max = 0;
+        sm.tie_col = ~0u;  // (not found: the tied value's lowest composite, still a valid bound)
+        for (int i = 0; i < 8; ++i) sm.tie_cnt[i] = 0;
 #ifdef DSTK_TIMING
         for (int i = 0; i < kTimingSlots; ++i) sm.ts[i] = 0;
 #endif
@@ -1885,6 +2038,14 @@ void topk_rows(Params p) {
     // tile is filtered against it, and a raise costs a sync and a locate.
     constexpr int kSeed = NV < CAP / kTileElems ? NV : CAP / kTileElems;
     static_assert(kSeed >= 1, "the seed tiles must fit an empty buffer");
+    static_assert(kSeed + 2 <= 8, "tie_cnt holds the seed tiles and two end tiles");
+    // The tied seed bound (crowded_seed_bound) is built into the bf16
+    // kernels only: runs of one value are the common case there (-inf
+    // padding, few distinct values), while in the fp32 kernels its mere
+    // presence costs the common path about a microsecond on the sampler
+    // shape (register allocation of the scan loop).  Tied fp32 rows are
+    // selected correctly all the same, through the overflow path.
+    constexpr bool kTiedSeed = EB == 2;
 
     // ---- buffer layout while scanning: buf[0, cbase) holds composites,
     // counted in the histogram; the free part is split into one region of R
@@ -1946,6 +2107,14 @@ void topk_rows(Params p) {
         // exactly the synced entries
         block_locate<WG, CAP>(sm, k, 0u, true);
         if (sm.loc_c[0] > 0) st.L = digit_floor(sm.loc_digit[0]);
+        if (kTiedSeed && sm.loc_c[0] >= kTiedBin) {
+            VecBases<kSeed> sb;
+#pragma unroll
+            for (int i = 0; i < kSeed; ++i) sb.b[i] = vb[i];
+            const SeedBound r = crowded_seed_bound<E, WG, CAP, kSeed>(sm, rsrc, sb, v0, v1, n, k, ntiles);
+            st.L = r.L;
+            st.exact = r.exact;
+        }
         pf.set(st.L);
         DSTK_T(sm, kPhSeed);
     };

@@ -64,6 +64,10 @@ def summarize(ts: np.ndarray) -> dict:
         return {k: float(np.mean(v)) for k, v in res.items()}
 
     out["segment_us"] = deltas(ts[~merger] if (~merger).any() else ts)
+    # the workgroup that ended last (its own phases, from its start)
+    slow = ts[np.argmax(ends)]
+    out["slowest_us"] = deltas(slow[None, :])
+    out["slowest_us"]["start_offset"] = float((slow[PH["start"]] - t0) * TICK_NS / 1e3)
     if merger.any():
         out["merger_us"] = deltas(ts[merger])
         last = ts[merger][np.argmax(ends[merger])]
@@ -128,7 +132,7 @@ def run(cfg: str, segs: int = 0, flags: int = 0, reps: int = 10, batch=None):
                                                                              w.sorted_index, w.return_value),
             "segments": plan.segments, "grid": plan.grid, "reps": reps,
             "span_us": round(float(np.mean([r["span_us"] for r in res])), 3),
-            "segment_us": avg("segment_us"), "merger_us": avg("merger_us"),
+            "segment_us": avg("segment_us"), "merger_us": avg("merger_us"), "slowest_us": avg("slowest_us"),
             "last_merge_path_us": avg("last_merge_path_us")}
 
 
@@ -136,13 +140,15 @@ def format_table(r: dict) -> str:
     lines = ["workload %s (%s): segments %d, grid %d, %d launches" % (
         r["workload"], r["shape"], r["segments"], r["grid"], r["reps"]),
         "mean launch span (first start to last end): %.2f us" % r["span_us"],
-        "%-14s %12s %12s %16s" % ("phase", "segment us", "merger us", "last merge path")]
+        "%-14s %12s %12s %16s %14s" % ("phase", "segment us", "merger us", "last merge path", "slowest wg")]
     for name in PHASES[1:]:
         s, m, p = r["segment_us"].get(name), r["merger_us"].get(name), r["last_merge_path_us"].get(name)
-        if s is None and m is None and p is None:
+        w = r["slowest_us"].get(name)
+        if s is None and m is None and p is None and w is None:
             continue
         f = lambda v: "%.3f" % v if v is not None else "-"
-        lines.append("%-14s %12s %12s %16s" % (name, f(s), f(m), f(p)))
+        lines.append("%-14s %12s %12s %16s %14s" % (name, f(s), f(m), f(p), f(w)))
+    lines.append("slowest workgroup started %.3f us after the first" % r["slowest_us"].get("start_offset", 0.0))
     if "kernel_start_to_merger_start" in r["last_merge_path_us"]:
         lines.append("last merger started %.3f us after the first workgroup" %
                      r["last_merge_path_us"]["kernel_start_to_merger_start"])
