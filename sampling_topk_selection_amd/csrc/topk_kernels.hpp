@@ -229,6 +229,7 @@ struct Smem {
     u32 tie_min, tie_max;  // seed: least and greatest key in the crowded bin
     u32 tie_col;           // seed: column of the tied k-th entry
     u32 tie_cnt[8];        // seed: the crowded bin's entries per bound tile
+    u32 pubseed;           // split row: the histogram holds the seed's publishing offsets
     u32 lwsum[16];       // block_locate: per-wave bin totals
     u32 lwfirst[16];     // block_locate: per-wave highest non-empty bin (waves with any)
     u64 trash[64];       // scan: written by the lanes that append nothing
@@ -1138,18 +1139,19 @@ constexpr u32 kSideMax = 16;
 // all of them (equal values, the high bits of small column numbers) cost
 // no level.  With kFixedFirst (32-bit keys, whose 11 bits below the top digit
 // seldom tie) the first level takes those bits right away and gathers the
-// OR and AND on the way, for the levels that may follow; there, a sub-bin
-// of at most kSideMax entries that still holds the k-th is settled
-// directly by side_select (with 16-bit keys the sub-bins that remain are
-// runs of equal values, seldom that small).  The histogram must be zero on
-// entry and is zero again on return.
+// OR and AND on the way, for the levels that may follow.  A sub-bin of at
+// most kSideMax entries that still holds the k-th is settled directly by
+// side_select (with 16-bit keys the first digit already takes high column
+// bits below the value's, so a tied value's entries spread over many
+// sub-bins).  The histogram must be zero on entry and is zero again on
+// return.
 template <int WG, int CAP, bool kFixedFirst = false>
 __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1) {
     if (r1 >= c1) return digit_floor(b1);  // the whole bin is kept
     const u32 tid = threadIdx.x, wave = tid / kWave;
     constexpr int kTop = 64 - kHistBits;
     constexpr int kSh1 = kTop - kHistBits;
-    if (kFixedFirst && tid == 0) sm.side_count = 0;  // (read after the barriers below)
+    if (tid == 0) sm.side_count = 0;  // (read after the barriers below)
     u64 P = digit_floor(b1);  // bits of T fixed so far: those at or above `fixed`
     int fixed = kTop;
     u32 r = r1;
@@ -1230,8 +1232,7 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         P |= A & (low_mask(lo1) & ~low_mask(hb2 + 1));  // the shared bits between the two parts
         fixed = sh2;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
-        if constexpr (kFixedFirst)
-            if (c <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
+        if (c <= kSideMax && (kFixedFirst || cnt <= 4096u)) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
         r = rr;
         D &= low_mask(sh2);
     }
@@ -2021,6 +2022,7 @@ void topk_rows(Params p) {
         sm.tie_min = ~0u;
         sm.tie_max = 0;
         sm.tie_col = ~0u;  // (not found: the tied value's lowest composite, still a valid bound)
+        sm.pubseed = 0;
         for (int i = 0; i < 8; ++i) sm.tie_cnt[i] = 0;
 #ifdef DSTK_TIMING
         for (int i = 0; i < kTimingSlots; ++i) sm.ts[i] = 0;
@@ -2105,9 +2107,27 @@ void topk_rows(Params p) {
         __syncthreads();
         // the locate also clears the histogram: from here on it counts
         // exactly the synced entries
-        block_locate<WG, CAP>(sm, k, 0u, true);
+        // A split row's segment that the seed covers whole (all its tiles are
+        // seed tiles) has its final histogram now: this locate also writes
+        // the publishing directory and bin offsets, and the tail publishes
+        // the appended entries straight from the regions (unless a rare
+        // round or the crowded path below needs the histogram back).
+        const u32 S_ = (u32)p.segs;
+        const bool pub_seed = S_ > 1 && ntiles <= (u32)kSeed;
+        if (pub_seed) {
+            const gptr<u32> dir = keep_g(p.ws_dir) + (u64)(row * S_ + seg) * kBins;
+            block_locate<WG, CAP, true>(sm, k, (k + S_ - 1) / S_, false, dir);
+            if (tid == 0) sm.pubseed = 1;
+        } else {
+            block_locate<WG, CAP>(sm, k, 0u, true);
+        }
         if (sm.loc_c[0] > 0) st.L = digit_floor(sm.loc_digit[0]);
         if (kTiedSeed && sm.loc_c[0] >= kTiedBin) {
+            if (pub_seed) {  // (the crowded path starts from an empty histogram)
+                for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
+                __syncthreads();
+                if (tid == 0) sm.pubseed = 0;
+            }
             VecBases<kSeed> sb;
 #pragma unroll
             for (int i = 0; i < kSeed; ++i) sb.b[i] = vb[i];
@@ -2124,12 +2144,21 @@ void topk_rows(Params p) {
     // step syncs and raises the bound.  Shorter segments keep the seed's
     // bound: a raise there costs more than the appends it saves, and a full
     // region raises the bound anyway.
-    auto process = [&](u32 t0, const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
+    // (first: the call for chunk 0, the only one a segment the seed covers
+    // whole makes; the loop's calls carry no code for that case)
+    auto process = [&](auto first, u32 t0, const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
         const u32 c = t0 / NV;
         const bool raise = t0 + NV < ntiles && c >= 7 && ((c + 1) & c) == 0;
         const u32 rtile = append_chunk<E, WG, NV, CAP>(sm, cx, st, pf, v, vb, 0u);
         const bool again = check_pending<WG, CAP>(sm, st, rtile < (u32)NV);
         if (again || raise) {
+            if constexpr (decltype(first)::value) {
+                if (sm.pubseed) {  // (the sync counts into an empty histogram)
+                    for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
+                    __syncthreads();
+                    if (tid == 0) sm.pubseed = 0;
+                }
+            }
             VecBases<NV> bases;
 #pragma unroll
             for (int i = 0; i < NV; ++i) bases.b[i] = vb[i];
@@ -2151,14 +2180,14 @@ void topk_rows(Params p) {
         issue(0, va, vba);
         issue(NV, vc, vbc);
         seed(va, vba);
-        process(0, va, vba);
+        process(std::true_type{}, 0, va, vba);
         if ((u32)NV < ntiles) {
             for (u32 t0 = NV;; t0 += 2 * NV) {
                 issue(t0 + NV, va, vba);
-                process(t0, vc, vbc);
+                process(std::false_type{}, t0, vc, vbc);
                 if (t0 + NV >= ntiles) break;
                 issue(t0 + 2 * NV, vc, vbc);
-                process(t0 + NV, va, vba);
+                process(std::false_type{}, t0 + NV, va, vba);
                 if (t0 + 2 * NV >= ntiles) break;
             }
         }
@@ -2172,10 +2201,21 @@ void topk_rows(Params p) {
     (void)timing;
     const int sorted = keep(p.sorted), retval = keep(p.retval), flags = keep(p.flags);
     const u32 S = keep((u32)p.segs);
+    const u32 cap = keep((u32)p.pub_cap);
+    // Published from the seed's bins?  (Not if more than the list holds.)
+    bool fast = false;
+    if (S > 1 && sm.pubseed) {
+        const u32 live0 = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
+        fast = live0 <= cap;
+        if (!fast) {  // (convert_regions counts into an empty histogram)
+            for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
+            __syncthreads();
+        }
+    }
     if (S == 1) {
         const u32 c = sync_regions<E, WG, CAP>(sm, st.cbase, st.R);
         if (tid == 0) sm.count = c;
-    } else {
+    } else if (!fast) {
         // a split row publishes from where the entries lie
         convert_regions<E, WG, CAP>(sm, st.cbase, st.R);
     }
@@ -2199,7 +2239,6 @@ void topk_rows(Params p) {
     // bin of its k-th counted entry or above) in descending top-digit order,
     // with a directory dir[j] = number of entries with top digit >= d_hi - j.
     const u32 slot = row * S + seg;
-    const u32 cap = keep((u32)p.pub_cap);
     const gptr<u64> ws_cand = keep_g(p.ws_cand);
     const gptr<u64> ws_meta = keep_g(p.ws_meta);
     const gptr<u32> ws_dir = keep_g(p.ws_dir);
@@ -2210,7 +2249,8 @@ void topk_rows(Params p) {
         const u32 q = (k + S - 1) / S;
         const gptr<u32> dir = ws_dir + (u64)slot * kBins;
         // locate, directory and placement offsets in one pass over the bins
-        block_locate<WG, CAP, true>(sm, k, q, false, dir);
+        // (done by the seed on the fast path)
+        if (!fast) block_locate<WG, CAP, true>(sm, k, q, false, dir);
         DSTK_T(sm, kPhLocate);
         u32 dl = sm.loc_c[0] ? sm.loc_digit[0] : 0u;
         u32 live = sm.loc_c[0] ? sm.loc_above[0] + sm.loc_c[0] : sm.loc_total;
@@ -2240,12 +2280,29 @@ void topk_rows(Params p) {
         }
         const gptr<u64> cand = ws_cand + (u64)slot * cap;
         const u32 total = moved ? cnt : map.total;
-        for (u32 i = tid; i < total; i += WG) {
-            const u64 e = sm.buf[moved ? i : map.addr(i)];
-            const u32 d = top_digit(e);
-            if (live > 0 && d >= dl) {
-                const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
-                if (pos < cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
+        if (fast) {
+            // the regions hold raw entries (bits << 32 | column): convert here
+            bool nan = false;
+            for (u32 i = tid; i < total; i += WG) {
+                const u64 raw = sm.buf[map.addr(i)];
+                const u32 bits = (u32)(raw >> 32);
+                nan |= E::is_nan(bits);
+                const u64 e = compose<E>(E::key(bits), (u32)raw);
+                const u32 d = top_digit(e);
+                if (live > 0 && d >= dl) {
+                    const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
+                    if (pos < cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
+                }
+            }
+            if (nan) sm.nan = 1;  // benign race: every writer stores 1
+        } else {
+            for (u32 i = tid; i < total; i += WG) {
+                const u64 e = sm.buf[moved ? i : map.addr(i)];
+                const u32 d = top_digit(e);
+                if (live > 0 && d >= dl) {
+                    const u32 pos = atomicAdd(&sm.hist[hidx(d)], 1u);
+                    if (pos < cap) st_agent(&cand[pos], e);  // pos < live by the histogram invariant
+                }
             }
         }
     }
