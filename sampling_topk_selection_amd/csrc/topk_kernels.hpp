@@ -2450,26 +2450,26 @@ void topk_rows(Params p) {
     }
     {
         for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;  // zero for the selection
-        constexpr int kLB = 4;  // loads in flight per thread
-        for (u32 base = 0; base < total; base += WG * kLB) {
-            u64 v[kLB];
+        // G threads per segment load its share (no search for the source)
+        const u32 G = (u32)WG / S;  // (S <= 256: two or more)
+        const u32 s_ = tid / G, j0 = tid - s_ * G;
+        if (s_ < S) {
+            const u32 off = sm.seg_count[s_];
+            const u32 share = (s_ + 1 < S ? sm.seg_count[s_ + 1] : total) - off;
+            const gptr<const u64> src = rc + (u64)s_ * cap;
+            constexpr int kLB = 4;  // loads in flight per thread
+            for (u32 j = j0; j < share; j += G * kLB) {
+                u64 v[kLB];
 #pragma unroll
-            for (int u = 0; u < kLB; ++u) {
-                const u32 f = base + u * WG + tid;
-                v[u] = 0;
-                if (f < total) {
-                    u32 lo = 0, hi = S;  // last segment whose offset is <= f
-                    while (hi - lo > 1) {
-                        const u32 mid = (lo + hi) >> 1;
-                        if (sm.seg_count[mid] <= f) lo = mid; else hi = mid;
-                    }
-                    v[u] = ld_agent(&rc[(u64)lo * cap + (f - sm.seg_count[lo])]);
+                for (int u = 0; u < kLB; ++u) {
+                    const u32 jj = j + (u32)u * G;
+                    v[u] = jj < share ? ld_agent(&src[jj]) : 0ull;
                 }
-            }
 #pragma unroll
-            for (int u = 0; u < kLB; ++u) {
-                const u32 f = base + u * WG + tid;
-                if (f < total) sm.buf[f] = v[u];
+                for (int u = 0; u < kLB; ++u) {
+                    const u32 jj = j + (u32)u * G;
+                    if (jj < share) sm.buf[off + jj] = v[u];
+                }
             }
         }
     }
