@@ -2042,12 +2042,14 @@ void topk_rows(Params p) {
     static_assert(kSeed >= 1, "the seed tiles must fit an empty buffer");
     static_assert(kSeed + 2 <= 8, "tie_cnt holds the seed tiles and two end tiles");
     // The tied seed bound (crowded_seed_bound) is built into the bf16
-    // kernels only: runs of one value are the common case there (-inf
-    // padding, few distinct values), while in the fp32 kernels its mere
-    // presence costs the common path about a microsecond on the sampler
-    // shape (register allocation of the scan loop).  Tied fp32 rows are
-    // selected correctly all the same, through the overflow path.
-    constexpr bool kTiedSeed = EB == 2;
+    // kernel for k <= 1024 only: runs of one value are common there (-inf
+    // padding, few distinct values), while elsewhere its mere presence costs
+    // the common path more than it saves (register allocation: about a
+    // microsecond on the fp32 sampler shape; in the bf16 k > 1024 kernel,
+    // already at 256 VGPRs, thirty more spills, +3 us on 256 x 32768 with
+    // k = 4096).  Tied rows there are selected correctly all the same,
+    // through the overflow path.
+    constexpr bool kTiedSeed = EB == 2 && CAP == 8192;
 
     // ---- buffer layout while scanning: buf[0, cbase) holds composites,
     // counted in the histogram; the free part is split into one region of R
