@@ -1773,25 +1773,11 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
     u32x4 bt[kB];
 #pragma unroll
     for (int i = 0; i < kB; ++i) bt[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(bvb[i] + (int)tid - v0) * 16u, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-        const u32x4 xs[1] = {bt[i]};
-#pragma unroll
-        for (int s_ = 0; s_ < SL::kSlots; ++s_) {
-            u32 bits, col;
-            bool valid;
-            SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
-            hist_add(sm.hist, top_digit(compose<E>(E::key(bits), col)), valid);
-        }
-    }
-    __syncthreads();
-    block_locate<WG, CAP>(sm, k, 0u, true);
-    SeedBound r{sm.loc_c[0] > 0 ? digit_floor(sm.loc_digit[0]) : 0ull, 0u};
-    if (sm.loc_c[0] < kTiedBin) return r;
-    // one value in bin b1?  (least and greatest key; the bin's entries per
-    // tile, tc[i] this thread's)
-    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0];
-    u32 kmin = ~0u, kmax = 0u, tc[kB];
+    // -inf padding is the common run: its bin holds -inf only (and NaN,
+    // reported anyway), so its entries per tile are counted on the way
+    const u32 kNegInf = E::key(E::kKeyBits == 16 ? 0xFF80u : 0xFF800000u);
+    const u32 dNegInf = top_digit(compose<E>(kNegInf, 0u));
+    u32 tc[kB];
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
         tc[i] = 0;
@@ -1801,29 +1787,58 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
             u32 bits, col;
             bool valid;
             SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
-            const u32 kk = E::key(bits);
-            if (valid && top_digit(compose<E>(kk, col)) == b1) {
-                kmin = kk < kmin ? kk : kmin;
-                kmax = kk > kmax ? kk : kmax;
-                ++tc[i];
-            }
+            const u32 d = top_digit(compose<E>(E::key(bits), col));
+            hist_add(sm.hist, d, valid);
+            tc[i] += valid && d == dNegInf ? 1u : 0u;
         }
     }
-    kmin = wave_min(kmin);
-    kmax = wave_max(kmax);
+    __syncthreads();
+    block_locate<WG, CAP>(sm, k, 0u, true);
+    SeedBound r{sm.loc_c[0] > 0 ? digit_floor(sm.loc_digit[0]) : 0ull, 0u};
+    if (sm.loc_c[0] < kTiedBin) return r;
+    // one value in bin b1?  (least and greatest key; the bin's entries per
+    // tile, tc[i] this thread's)
+    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0];
+    u32 key = kNegInf;
+    if (b1 != dNegInf) {
+        u32 kmin = ~0u, kmax = 0u;
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            tc[i] = 0;
+            const u32x4 xs[1] = {bt[i]};
+#pragma unroll
+            for (int s_ = 0; s_ < SL::kSlots; ++s_) {
+                u32 bits, col;
+                bool valid;
+                SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
+                const u32 kk = E::key(bits);
+                if (valid && top_digit(compose<E>(kk, col)) == b1) {
+                    kmin = kk < kmin ? kk : kmin;
+                    kmax = kk > kmax ? kk : kmax;
+                    ++tc[i];
+                }
+            }
+        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
+        if (lane_id() == 0) {
+            atomicMin(&sm.tie_min, kmin);
+            atomicMax(&sm.tie_max, kmax);
+        }
+    }
     u32 wc[kB];
 #pragma unroll
     for (int i = 0; i < kB; ++i) wc[i] = __builtin_amdgcn_readlane(wave_incl_scan(tc[i]), kWave - 1);
     if (lane_id() == 0) {
-        atomicMin(&sm.tie_min, kmin);
-        atomicMax(&sm.tie_max, kmax);
 #pragma unroll
         for (int i = 0; i < kB; ++i)
             if (wc[i]) atomicAdd(&sm.tie_cnt[i], wc[i]);
     }
     __syncthreads();
-    const u32 key = sm.tie_min;
-    if (key != sm.tie_max) return r;
+    if (b1 != dNegInf) {
+        key = sm.tie_min;
+        if (key != sm.tie_max) return r;
+    }
     // the tile holding the r1-th lowest column of the bin: tiles are whole
     // column ranges, so order them by start
     u32 mine = 0, rr = 0;
@@ -1838,6 +1853,21 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
             rr = r1 - below;
             which = i;
         }
+    }
+    // a tile of the bin's entries only: the r-th lowest column is the tile's
+    // r-th (the common case for a run of one value), with no scan
+    constexpr u32 kTileElems = (u32)kTileVecs * E::kPerVec;
+    int whole = -1;
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+        if (i == which && sm.tie_cnt[i] == kTileElems) whole = i;
+    if (whole >= 0) {
+        int vbw = 0;
+#pragma unroll
+        for (int i = 0; i < kB; ++i) vbw = i == whole ? bvb[i] : vbw;
+        r.L = compose<E>(key, (u32)vbw * E::kPerVec + rr - 1u);
+        r.exact = 1u;
+        return r;
     }
     // inside it, column order is thread order, then slot order
     u32 tot;
