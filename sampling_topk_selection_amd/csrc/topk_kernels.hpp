@@ -2031,13 +2031,23 @@ void topk_rows(Params p) {
     const u32 ntiles = (u32)((v1 - v0 + kTileVecs - 1) / kTileVecs);
 
     // Tile visiting order: t -> (a t + b) mod ntiles with gcd(a, ntiles) = 1.
+    // The bf16 kernel for k > 1024 first visits the segment's last and
+    // first tiles, then tiles 1 .. ntiles - 2 in that permuted order: with k
+    // an eighth of a row or more, a seed drawn from the middle of a sorted
+    // or padded row (ascending scores, a -inf tail) admits most of the row,
+    // and the sync, refine and emit then work on up to the buffer's size.
+    // (Elsewhere the fixed positions cost more than they save: every
+    // workgroup's first loads then fall at one offset of its segment.)
+    constexpr bool kEndsFirst = EB == 2 && CAP > 8192;
+    const bool ends = kEndsFirst && ntiles > 2;
+    const u32 m = ends ? ntiles - 2 : ntiles;  // tiles in the permuted part
     const u32 h = hash32(blockIdx.x * 0x9E3779B9u ^ p.seed);
     u32 a = 1, b = 0;
-    if (ntiles > 1) {
-        a = (u32)(((u64)ntiles * 0x9E3779B9ull) >> 32) | 1u;
-        if (a >= ntiles) a = 1;
-        while (gcd_u32(a, ntiles) != 1) ++a;
-        b = h % ntiles;
+    if (m > 1) {
+        a = (u32)(((u64)m * 0x9E3779B9ull) >> 32) | 1u;
+        if (a >= m) a = 1;
+        while (gcd_u32(a, m) != 1) ++a;
+        b = h % m;
     }
 
     for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
@@ -2064,7 +2074,7 @@ void topk_rows(Params p) {
     pf.set(0ull);
     __syncthreads();
 
-    u32 pr = b;  // permuted index of the next tile to request
+    u32 pr = b;  // permuted index of the next tile to request (of the permuted part)
     // Tiles counted to seed the bound: the whole first chunk, as far as an
     // empty buffer holds it.  A tighter seed pays for itself: every later
     // tile is filtered against it, and a raise costs a sync and a locate.
@@ -2094,11 +2104,20 @@ void topk_rows(Params p) {
     auto issue = [&](u32 t0, u32x4 (&v)[NV], int (&vb)[NV]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            vb[i] = t0 + (u32)i < ntiles ? v0 + (int)pr * kTileVecs : v1;
+            const u32 t = t0 + (u32)i;  // visiting position
+            u32 tile = pr;
+            bool step = true;
+            if constexpr (kEndsFirst) {
+                step = !ends || t >= 2u;
+                tile = step ? pr + (ends ? 1u : 0u) : (t == 0u ? ntiles - 1u : 0u);
+            }
+            vb[i] = t < ntiles ? v0 + (int)tile * kTileVecs : v1;
             v[i] = load_vec(vb[i] + (int)tid);
             __builtin_amdgcn_sched_barrier(0);  // keep requests in slot order
-            pr += a;
-            if (pr >= ntiles) pr -= ntiles;
+            if (step) {
+                pr += a;
+                if (pr >= m) pr -= m;
+            }
         }
     };
     // Seed: count every element of the first kSeed tiles and take the bin
