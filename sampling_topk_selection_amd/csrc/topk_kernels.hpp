@@ -1774,7 +1774,9 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
 #pragma unroll
     for (int i = 0; i < kB; ++i) bt[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(bvb[i] + (int)tid - v0) * 16u, 0, 0);
     // -inf padding is the common run: its bin holds -inf only (and NaN,
-    // reported anyway), so its entries per tile are counted on the way
+    // reported anyway), so its entries per tile are counted on the way, in
+    // registers, and added to the histogram once per wave (atomics that
+    // every wave aims at one word are serialized)
     const u32 kNegInf = E::key(E::kKeyBits == 16 ? 0xFF80u : 0xFF800000u);
     const u32 dNegInf = top_digit(compose<E>(kNegInf, 0u));
     u32 tc[kB];
@@ -1788,10 +1790,19 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
             bool valid;
             SL::get(xs, s_, bvb[i], tid, v1, n, bits, col, valid);
             const u32 d = top_digit(compose<E>(E::key(bits), col));
-            hist_add(sm.hist, d, valid);
-            tc[i] += valid && d == dNegInf ? 1u : 0u;
+            const bool ninf = valid && d == dNegInf;
+            hist_add(sm.hist, d, valid && !ninf);
+            tc[i] += ninf ? 1u : 0u;
         }
     }
+    u32 wc[kB];  // the wave's -inf entries per tile
+    u32 wn = 0;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        wc[i] = __builtin_amdgcn_readlane(wave_incl_scan(tc[i]), kWave - 1);
+        wn += wc[i];
+    }
+    if (lane_id() == 0 && wn) atomicAdd(&sm.hist[hidx(dNegInf)], wn);
     __syncthreads();
     block_locate<WG, CAP>(sm, k, 0u, true);
     SeedBound r{sm.loc_c[0] > 0 ? digit_floor(sm.loc_digit[0]) : 0ull, 0u};
@@ -1825,10 +1836,9 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
             atomicMin(&sm.tie_min, kmin);
             atomicMax(&sm.tie_max, kmax);
         }
-    }
-    u32 wc[kB];
 #pragma unroll
-    for (int i = 0; i < kB; ++i) wc[i] = __builtin_amdgcn_readlane(wave_incl_scan(tc[i]), kWave - 1);
+        for (int i = 0; i < kB; ++i) wc[i] = __builtin_amdgcn_readlane(wave_incl_scan(tc[i]), kWave - 1);
+    }
     if (lane_id() == 0) {
 #pragma unroll
         for (int i = 0; i < kB; ++i)
@@ -2124,26 +2134,12 @@ void topk_rows(Params p) {
     // edge of the k-th counted as the bound; those tiles are then appended
     // like the others.
     auto seed = [&](const u32x4 (&v)[NV], const int (&vb)[NV]) __attribute__((always_inline)) {
-        auto count = [&](auto agg_tag) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < kSeed; ++i) {
-                const u32x4 xs[1] = {v[i]};
-#pragma unroll
-                for (int s = 0; s < SL::kSlots; ++s) {
-                    u32 bits, col;
-                    bool valid;
-                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
-                    const u32 d = top_digit(compose<E>(E::key(bits), col));
-                    if constexpr (decltype(agg_tag)::value)
-                        hist_add(sm.hist, d, valid);
-                    else if (valid)
-                        atomicAdd(&sm.hist[hidx(d)], 1u);
-                }
-            }
-        };
         // Runs of equal values (padding, quantized scores) put whole waves
-        // in one bin: then count by wave where the lanes agree.  The wave's
-        // first elements decide, for its whole seed.
+        // in one bin: then the wave counts the entries of each tile that
+        // fall in the bin of the tile's first element in a register, adds
+        // them once per tile (atomics that every wave aims at one word are
+        // serialized) and only the others one by one.  The wave's first
+        // elements decide, for its whole seed.
         u32 b0, c0;
         bool ok0;
         {
@@ -2151,6 +2147,29 @@ void topk_rows(Params p) {
             SL::get(xs, 0, vb[0], tid, v1, n, b0, c0, ok0);
         }
         const u32 d0 = top_digit(compose<E>(E::key(b0), c0));
+        auto count = [&](auto agg_tag) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kSeed; ++i) {
+                const u32x4 xs[1] = {v[i]};
+                u32 run = 0, nrun = 0;
+#pragma unroll
+                for (int s = 0; s < SL::kSlots; ++s) {
+                    u32 bits, col;
+                    bool valid;
+                    SL::get(xs, s, vb[i], tid, v1, n, bits, col, valid);
+                    const u32 d = top_digit(compose<E>(E::key(bits), col));
+                    if constexpr (decltype(agg_tag)::value) {
+                        if (s == 0) run = __builtin_amdgcn_readfirstlane(d);
+                        nrun += (u32)__popcll(__ballot(valid && d == run));
+                        if (valid && d != run) atomicAdd(&sm.hist[hidx(d)], 1u);
+                    } else if (valid) {
+                        atomicAdd(&sm.hist[hidx(d)], 1u);
+                    }
+                }
+                if constexpr (decltype(agg_tag)::value)
+                    if (lane_id() == 0 && nrun) atomicAdd(&sm.hist[hidx(run)], nrun);
+            }
+        };
         if (__ballot(ok0) == ~0ull && __ballot(d0 != __builtin_amdgcn_readfirstlane(d0)) == 0)
             count(std::true_type{});
         else
