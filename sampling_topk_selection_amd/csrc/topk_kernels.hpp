@@ -1137,16 +1137,19 @@ constexpr u32 kSideMax = 16;
 // from their OR and AND): the highest run of such bits and, when it is
 // shorter than 11, the next such bits below it, so runs of bits shared by
 // all of them (equal values, the high bits of small column numbers) cost
-// no level.  With kFixedFirst (32-bit keys, whose 11 bits below the top digit
-// seldom tie) the first level takes those bits right away and gathers the
-// OR and AND on the way, for the levels that may follow.  A sub-bin of at
-// most kSideMax entries that still holds the k-th is settled directly by
-// side_select (with 16-bit keys the first digit already takes high column
-// bits below the value's, so a tied value's entries spread over many
-// sub-bins).  The histogram must be zero on entry and is zero again on
-// return.
-template <int WG, int CAP, bool kFixedFirst = false>
-__device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1) {
+// no level.  With a fixed first level the digit's bits are known in advance
+// and it is counted in the same pass that gathers the OR and AND (for the
+// levels that may follow): kFirst 1, 32-bit keys, whose 11 bits below the
+// top digit seldom tie: those bits; kFirst 2, 16-bit keys (composite = key
+// << 48 | ~column << 16, columns below 2^cb): the key's 5 bits below the top
+// digit and the column's highest min(6, cb) bits, the bits between them
+// being ones for every such column.  A sub-bin of at most kSideMax entries
+// that still holds the k-th is settled directly by side_select (with
+// 16-bit keys the first digit already takes high column bits below the
+// value's, so a tied value's entries spread over many sub-bins).  The
+// histogram must be zero on entry and is zero again on return.
+template <int WG, int CAP, int kFirst = 0>
+__device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 cb = 0) {
     if (r1 >= c1) return digit_floor(b1);  // the whole bin is kept
     const u32 tid = threadIdx.x, wave = tid / kWave;
     constexpr int kTop = 64 - kHistBits;
@@ -1156,15 +1159,21 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
     int fixed = kTop;
     u32 r = r1;
     u64 o = 0, a = ~0ull;
+    // kFirst 2: the column part's length and position
+    const u32 len2 = cb < 6u ? cb : 6u;
+    const int csh = 16 + (int)cb - (int)len2;
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
         if (top_digit(e) == b1) {
             o |= e;
             a &= e;
-            if constexpr (kFixedFirst) atomicAdd(&sm.hist[hidx((u32)(e >> kSh1) & (kBins - 1))], 1u);
+            if constexpr (kFirst == 1) atomicAdd(&sm.hist[hidx((u32)(e >> kSh1) & (kBins - 1))], 1u);
+            if constexpr (kFirst == 2)
+                atomicAdd(&sm.hist[hidx((((u32)(e >> 48) & 31u) << len2) | ((u32)(e >> csh) & ((1u << len2) - 1u)))],
+                          1u);
         }
     }
-    if constexpr (kFixedFirst) {
+    if constexpr (kFirst == 1) {
         __syncthreads();
         block_locate<WG, CAP>(sm, r1, 0u, true);
         P |= (u64)sm.loc_digit[0] << kSh1;
@@ -1172,6 +1181,16 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         r = sm.loc_r[0];
         if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
         if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(kSh1), P, r);
+    }
+    if constexpr (kFirst == 2) {
+        __syncthreads();
+        block_locate<WG, CAP>(sm, r1, 0u, true);
+        const u32 d = sm.loc_digit[0];
+        P |= ((u64)(d >> len2) << 48) | ((u64)(d & ((1u << len2) - 1u)) << csh) | (low_mask(48) & ~low_mask(16 + (int)cb));
+        fixed = csh;
+        r = sm.loc_r[0];
+        if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
+        if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(csh), P, r);
     }
     {
         const u32 ohi = wave_or((u32)(o >> 32)), olo = wave_or((u32)o);
@@ -1232,7 +1251,7 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         P |= A & (low_mask(lo1) & ~low_mask(hb2 + 1));  // the shared bits between the two parts
         fixed = sh2;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
-        if (c <= kSideMax && (kFixedFirst || cnt <= 4096u)) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
+        if (c <= kSideMax && (kFirst != 0 || cnt <= 4096u)) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
         r = rr;
         D &= low_mask(sh2);
     }
@@ -1911,7 +1930,7 @@ __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, 
                                              int sorted, int retval, int flags, gptr<void> row_idx_p, gptr<void> row_val,
                                              gptr<int32_t> flag, int32_t flag_value, u64* timing) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
-    const u64 T = refine<WG, CAP, E::kKeyBits == 32>(sm, cnt, b1, r1, c1);
+    const u64 T = refine<WG, CAP, E::kKeyBits == 32 ? 1 : 2>(sm, cnt, b1, r1, c1, n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u);
     DSTK_T(sm, kPhRefine);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
