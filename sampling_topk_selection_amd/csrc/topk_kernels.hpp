@@ -1802,6 +1802,17 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buf
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
         tc[i] = 0;
+        // the wave's part of the tile past the segment, or -inf throughout
+        // with every column valid: counted at once
+        const int vi = bvb[i] + (int)tid;
+        if (__ballot(vi < v1) == 0) continue;
+        const u32 pat = E::kKeyBits == 16 ? 0xFF80FF80u : 0xFF800000u;
+        const bool ninf_all = vi < v1 && (u32)vi * E::kPerVec + (E::kPerVec - 1) < n && bt[i][0] == pat &&
+                              bt[i][1] == pat && bt[i][2] == pat && bt[i][3] == pat;
+        if (__ballot(ninf_all) == ~0ull) {
+            tc[i] = E::kPerVec;
+            continue;
+        }
         const u32x4 xs[1] = {bt[i]};
 #pragma unroll
         for (int s_ = 0; s_ < SL::kSlots; ++s_) {
@@ -2158,7 +2169,9 @@ void topk_rows(Params p) {
         // fall in the bin of the tile's first element in a register, adds
         // them once per tile (atomics that every wave aims at one word are
         // serialized) and only the others one by one.  The wave's first
-        // elements decide, for its whole seed.
+        // elements decide, for its whole seed; in the bf16 kernels a wave's
+        // part of a tile that holds one value throughout is counted at once
+        // either way.
         u32 b0, c0;
         bool ok0;
         {
@@ -2171,6 +2184,20 @@ void topk_rows(Params p) {
             for (int i = 0; i < kSeed; ++i) {
                 const u32x4 xs[1] = {v[i]};
                 u32 run = 0, nrun = 0;
+                if constexpr (EB == 2) {
+                    // the wave's part of the tile one value throughout, every
+                    // column valid (a run of padding): counted at once
+                    const int vi = vb[i] + (int)tid;
+                    const u32 b0 = __builtin_amdgcn_readfirstlane(v[i][0] & 0xFFFFu);
+                    const u32 pat = b0 | (b0 << 16);
+                    const bool one = vi < v1 && (u32)vi * E::kPerVec + (E::kPerVec - 1) < n && v[i][0] == pat &&
+                                     v[i][1] == pat && v[i][2] == pat && v[i][3] == pat;
+                    if (__ballot(one) == ~0ull) {
+                        if (lane_id() == 0)
+                            atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(b0), 0u)))], (u32)(kWave * E::kPerVec));
+                        continue;
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < SL::kSlots; ++s) {
                     u32 bits, col;
