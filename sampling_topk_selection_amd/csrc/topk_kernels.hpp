@@ -1772,9 +1772,20 @@ struct SeedBound {
 // against it; otherwise the bin's floor.  The histogram is zero on entry and
 // on return.  Out of line, so the common path keeps its registers.
 template <class E, int WG, int CAP, int KS>
-__device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, __amdgpu_buffer_rsrc_t rsrc, VecBases<KS> sb,
+__device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, const uint8_t* seg, VecBases<KS> sb,
                                                      int v0, int v1, u32 n, u32 k, u32 ntiles) {
     using SL = Slot<E, 1, WG>;
+    // the segment as a buffer resource again, from wave-uniform values (the
+    // arguments of a call arrive in vector registers, and loads through a
+    // descriptor held there are issued lane group by lane group)
+    // (the builtin returns int: each half goes through u32, so the low half
+    // is not sign-extended into the high one)
+    const u64 sa = (u64)seg;
+    const u64 hi = (u32)__builtin_amdgcn_readfirstlane((int)(u32)(sa >> 32));
+    const u64 lo = (u32)__builtin_amdgcn_readfirstlane((int)(u32)sa);
+    const uint8_t* seg_u = (const uint8_t*)((hi << 32) | lo);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)seg_u, (short)0, (int)((u32)(__builtin_amdgcn_readfirstlane(v1 - v0)) * 16u), kBufferWord3);
     constexpr int kB = KS + 2;
     constexpr int kTileVecs = WG;
     const u32 tid = threadIdx.x;
@@ -2247,7 +2258,8 @@ void topk_rows(Params p) {
             VecBases<kSeed> sb;
 #pragma unroll
             for (int i = 0; i < kSeed; ++i) sb.b[i] = vb[i];
-            const SeedBound r = crowded_seed_bound<E, WG, CAP, kSeed>(sm, rsrc, sb, v0, v1, n, k, ntiles);
+            const SeedBound r =
+                crowded_seed_bound<E, WG, CAP, kSeed>(sm, row_in + (int64_t)v0 * 16, sb, v0, v1, n, k, ntiles);
             st.L = r.L;
             st.exact = r.exact;
         }
