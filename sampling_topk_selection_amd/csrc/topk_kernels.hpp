@@ -1186,7 +1186,8 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         __syncthreads();
         block_locate<WG, CAP>(sm, r1, 0u, true);
         const u32 d = sm.loc_digit[0];
-        P |= ((u64)(d >> len2) << 48) | ((u64)(d & ((1u << len2) - 1u)) << csh) | (low_mask(48) & ~low_mask(16 + (int)cb));
+        P |= ((u64)(d >> len2) << 48) | ((u64)(d & ((1u << len2) - 1u)) << csh) |
+             (low_mask(48) & ~low_mask(16 + (int)cb));
         fixed = csh;
         r = sm.loc_r[0];
         if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
@@ -1251,7 +1252,8 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         P |= A & (low_mask(lo1) & ~low_mask(hb2 + 1));  // the shared bits between the two parts
         fixed = sh2;
         if (rr >= c) return P;  // the whole sub-bin is kept: T is its least possible key
-        if (c <= kSideMax && (kFirst != 0 || cnt <= 4096u)) return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
+        if (c <= kSideMax && (kFirst != 0 || cnt <= 4096u))
+            return side_select<WG, CAP>(sm, cnt, ~low_mask(sh2), P, rr);
         r = rr;
         D &= low_mask(sh2);
     }
@@ -1952,7 +1954,8 @@ __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, 
                                              int sorted, int retval, int flags, gptr<void> row_idx_p, gptr<void> row_val,
                                              gptr<int32_t> flag, int32_t flag_value, u64* timing) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
-    const u64 T = refine<WG, CAP, E::kKeyBits == 32 ? 1 : 2>(sm, cnt, b1, r1, c1, n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u);
+    const u32 cb = n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u;  // column bits
+    const u64 T = refine<WG, CAP, E::kKeyBits == 32 ? 1 : 2>(sm, cnt, b1, r1, c1, cb);
     DSTK_T(sm, kPhRefine);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
@@ -2199,13 +2202,14 @@ void topk_rows(Params p) {
                     // the wave's part of the tile one value throughout, every
                     // column valid (a run of padding): counted at once
                     const int vi = vb[i] + (int)tid;
-                    const u32 b0 = __builtin_amdgcn_readfirstlane(v[i][0] & 0xFFFFu);
-                    const u32 pat = b0 | (b0 << 16);
+                    const u32 first = __builtin_amdgcn_readfirstlane(v[i][0] & 0xFFFFu);
+                    const u32 pat = first | (first << 16);
                     const bool one = vi < v1 && (u32)vi * E::kPerVec + (E::kPerVec - 1) < n && v[i][0] == pat &&
                                      v[i][1] == pat && v[i][2] == pat && v[i][3] == pat;
                     if (__ballot(one) == ~0ull) {
                         if (lane_id() == 0)
-                            atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(b0), 0u)))], (u32)(kWave * E::kPerVec));
+                            atomicAdd(&sm.hist[hidx(top_digit(compose<E>(E::key(first), 0u)))],
+                                      (u32)(kWave * E::kPerVec));
                         continue;
                     }
                 }
