@@ -64,6 +64,9 @@ constexpr int kWave = 64;
 // Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle,
 // no index stride): byte-addressed loads with a range check.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of the scan's loads: non-temporal (each input line is read
+// once; measured on a plain 33 MB read over 256 workgroups: 6.9 -> 6.3 us).
+constexpr int kScanAux = 2;
 // A segment is addressed by one buffer resource: at most 2^27 vectors (2 GiB).
 constexpr int kMaxSegVecs = 1 << 27;
 
@@ -260,15 +263,23 @@ enum Phase : int {
     kTimingSlots = 16
 };
 #ifdef DSTK_TIMING
-#define DSTK_T(sm, id)                                     \
-    do {                                                   \
-        if (threadIdx.x == 0) (sm).ts[id] = wall_clock64(); \
+// Slots kClkStart / kClkEnd hold the shader clock counter (s_memtime) at
+// entry and at the flush, for the workgroup's mean shader clock rate.
+constexpr int kClkStart = 13, kClkEnd = 14;
+#define DSTK_T(sm, id)                                                  \
+    do {                                                                \
+        if (threadIdx.x == 0) {                                         \
+            (sm).ts[id] = wall_clock64();                               \
+            if ((id) == kPhStart) (sm).ts[kClkStart] = clock64();       \
+        }                                                               \
     } while (0)
 #define DSTK_T_FLUSH(sm, timing)                                                      \
     do {                                                                              \
-        if (threadIdx.x == 0 && (timing))                                             \
+        if (threadIdx.x == 0 && (timing)) {                                           \
+            (sm).ts[kClkEnd] = clock64();                                             \
             for (int i_ = 0; i_ < kTimingSlots; ++i_)                                 \
                 (timing)[(uint64_t)blockIdx.x * kTimingSlots + i_] = (sm).ts[i_];     \
+        }                                                                             \
     } while (0)
 #else
 #define DSTK_T(sm, id) ((void)0)
@@ -2080,7 +2091,7 @@ void topk_rows(Params p) {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(row_in + (int64_t)v0 * 16), (short)0, (int)((u32)(v1 - v0) * 16u), kBufferWord3);
     auto load_vec = [&](int vi) -> u32x4 {  // vi: absolute vector index in the row
-        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(vi - v0) * 16u, 0, 0);
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (u32)(vi - v0) * 16u, 0, kScanAux);
     };
     const u32 ntiles = (u32)((v1 - v0 + kTileVecs - 1) / kTileVecs);
 

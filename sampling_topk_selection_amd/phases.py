@@ -30,6 +30,7 @@ SLOTS = 16
 PHASES = ["start", "seed", "scan", "sync", "locate", "(unused)", "publish", "ticket", "metadata", "row_bin",
           "list_load", "refine", "emit"]
 PH = {name: i for i, name in enumerate(PHASES)}
+CLK_START, CLK_END = 13, 14  # shader clock counter at entry and at the flush
 
 
 def _load(builder):
@@ -47,10 +48,17 @@ def summarize(ts: np.ndarray) -> dict:
     """ts: [grid, SLOTS] int64 timestamps of one launch (0 = not noted)."""
     used = ts[:, PH["start"]] != 0
     ts = ts[used]
+    clk = ts[:, CLK_START:CLK_END + 1].astype(np.float64)
+    ts = ts[:, :len(PHASES)]
     t0 = ts[:, PH["start"]].min()
     ends = ts.max(axis=1)
+    # mean shader clock over each workgroup's life: shader clock ticks over
+    # constant-clock ticks, from entry to the last note
+    ok = (clk[:, 1] > clk[:, 0]) & (ends > ts[:, PH["start"]])
+    mhz = (clk[ok, 1] - clk[ok, 0]) / ((ends[ok] - ts[ok, PH["start"]]) * TICK_NS * 1e-3)
     merger = ts[:, PH["metadata"]] != 0
     out = {"workgroups": int(ts.shape[0]), "span_us": float((ends.max() - t0) * TICK_NS / 1e3),
+           "clock_mhz": float(np.mean(mhz)) if ok.any() else 0.0,
            "mergers": int(merger.sum())}
 
     def deltas(rows):
@@ -132,6 +140,7 @@ def run(cfg: str, segs: int = 0, flags: int = 0, reps: int = 10, batch=None):
                                                                              w.sorted_index, w.return_value),
             "segments": plan.segments, "grid": plan.grid, "reps": reps,
             "span_us": round(float(np.mean([r["span_us"] for r in res])), 3),
+            "clock_mhz": round(float(np.mean([r["clock_mhz"] for r in res])), 1),
             "segment_us": avg("segment_us"), "merger_us": avg("merger_us"), "slowest_us": avg("slowest_us"),
             "last_merge_path_us": avg("last_merge_path_us")}
 
@@ -139,7 +148,8 @@ def run(cfg: str, segs: int = 0, flags: int = 0, reps: int = 10, batch=None):
 def format_table(r: dict) -> str:
     lines = ["workload %s (%s): segments %d, grid %d, %d launches" % (
         r["workload"], r["shape"], r["segments"], r["grid"], r["reps"]),
-        "mean launch span (first start to last end): %.2f us" % r["span_us"],
+        "mean launch span (first start to last end): %.2f us; mean shader clock %.0f MHz" % (
+            r["span_us"], r["clock_mhz"]),
         "%-14s %12s %12s %16s %14s" % ("phase", "segment us", "merger us", "last merge path", "slowest wg")]
     for name in PHASES[1:]:
         s, m, p = r["segment_us"].get(name), r["merger_us"].get(name), r["last_merge_path_us"].get(name)
