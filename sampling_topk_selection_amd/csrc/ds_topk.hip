@@ -337,12 +337,19 @@ int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_str
         hipError_t e;
         if (small) {
             const int64_t grid = (rows + kSmallRows - 1) / kSmallRows;
-            if (dtype == DS_DTYPE_BF16)
-                hipLaunchKernelGGL(dstk::topk_small_rows<2>, dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0, stream,
-                                   prm, rows);
+            const bool tiny = n <= dstk::kTinyN;
+            if (dtype == DS_DTYPE_BF16 && tiny)
+                hipLaunchKernelGGL((dstk::topk_small_rows<2, 8>), dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0,
+                                   stream, prm, rows);
+            else if (dtype == DS_DTYPE_BF16)
+                hipLaunchKernelGGL((dstk::topk_small_rows<2, dstk::kHistBits>), dim3((uint32_t)grid),
+                                   dim3(dstk::kSmallWG), 0, stream, prm, rows);
+            else if (tiny)
+                hipLaunchKernelGGL((dstk::topk_small_rows<4, 8>), dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0,
+                                   stream, prm, rows);
             else
-                hipLaunchKernelGGL(dstk::topk_small_rows<4>, dim3((uint32_t)grid), dim3(dstk::kSmallWG), 0, stream,
-                                   prm, rows);
+                hipLaunchKernelGGL((dstk::topk_small_rows<4, dstk::kHistBits>), dim3((uint32_t)grid),
+                                   dim3(dstk::kSmallWG), 0, stream, prm, rows);
             e = hipGetLastError();
         } else {
             e = launch(pl, prm, rows, stream);

@@ -2630,23 +2630,36 @@ namespace dstk {
 // Rows of at most kSmallN columns: one wave per row, kSmallWG / 64 rows per
 // workgroup (the one-workgroup-per-row kernel would leave most of a 512-lane
 // workgroup idle).  Lane l keeps the composites of columns l, l + 64, ... in
-// registers; a radix select over 11-bit digits, in the wave's own LDS
+// registers; a radix select over kB-bit digits, in the wave's own LDS
 // histogram, narrows the k-th composite from the top bits down until its
 // digit's whole sub-bin is kept, which gives T with exactly k composites at
-// or above it.  Kept entries are written in column order by ballot (that is
-// index order too), or gathered and sorted by value.  Only the wave's own
-// LDS is touched, so no workgroup barrier is needed.
+// or above it; between levels the window moves past the bits that every
+// remaining candidate shares (their OR and AND), so runs of equal bits
+// (high column bits, tied values) cost no level.  Kept entries are written
+// in column order by ballot (that is index order too), or gathered and
+// sorted by value.  Only the wave's own LDS is touched, so no workgroup
+// barrier is needed.  Two instances: 11-bit digits for rows up to kSmallN
+// columns, and 8-bit digits with a quarter of the LDS per wave for rows up
+// to kTinyN (a 2048-bin histogram to clear and scan per level, for a few
+// elements per lane, and 8 KB per wave that limit how many waves a CU
+// holds, cost more than a level or two more).
 constexpr int kSmallN = 2048;
+constexpr int kTinyN = 256;
 constexpr int kSmallWG = 256;
-constexpr int kSmallJ = kSmallN / kWave;         // columns per lane
 constexpr int kSmallValueMax = kBins / 2;        // value order: k the LDS list holds (u64 in the histogram)
 
-template <int EB>
+template <int EB, int kB>
 __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t rows) {
     using E = Elem<EB>;
     using VT = typename std::conditional<EB == 2, uint16_t, uint32_t>::type;
     constexpr u32 kWaves = kSmallWG / kWave;
-    __shared__ u32 hist_all[kWaves][kBins];
+    constexpr u32 kNB = 1u << kB;                            // digit bins
+    constexpr u32 kPerLane = kNB / kWave;                    // bins a lane sums
+    constexpr int kSmallJ = (kB == kHistBits ? kSmallN : kTinyN) / kWave;  // columns per lane
+    // the histogram, and for value order the list of kept composites (u64)
+    constexpr u32 kWords = kB == kHistBits ? (u32)kBins : 2u * (u32)kTinyN;
+    static_assert(kPerLane >= 1 && kPerLane <= (u32)kWave && kWords >= kNB, "digit bins per lane");
+    __shared__ u32 hist_all[kWaves][kWords];
     const u32 wave = threadIdx.x / kWave, l = lane_id();
     const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
     if (row >= rows) return;  // the whole wave
@@ -2688,31 +2701,48 @@ __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t ro
     u64 P = 0;
     int fixed = 64;
     u32 r = k;
-    for (int level = 0; level < 64 / kHistBits + 1; ++level) {
-        const int sh = fixed > kHistBits ? fixed - kHistBits : 0;
+    for (int level = 0; level < 64; ++level) {
+        const int sh = fixed > kB ? fixed - kB : 0;
         const u64 pm = ~low_mask(fixed), wm = low_mask(fixed - sh);
-        for (u32 i = l; i < (u32)kBins; i += kWave) hist[i] = 0;
+        for (u32 i = l; i < kNB; i += kWave) hist[i] = 0;
 #pragma unroll
         for (u32 j = 0; j < (u32)kSmallJ; ++j)
             if (j < jn && comp[j] != 0 && (comp[j] & pm) == P) atomicAdd(&hist[(u32)((comp[j] >> sh) & wm)], 1u);
-        // lane l owns digits 2047 - 32 l - i, i < 32 (descending with the lane)
+        // lane l owns digits kNB - 1 - kPerLane l - i, i < kPerLane
+        // (descending with the lane)
         u32 s = 0;
 #pragma unroll
-        for (u32 i = 0; i < 32u; ++i) s += hist[kBins - 1u - 32u * l - i];
+        for (u32 i = 0; i < kPerLane; ++i) s += hist[kNB - 1u - kPerLane * l - i];
         const u32 incl = wave_incl_scan(s);
         const u64 hm = __ballot(incl >= r);  // not empty: r <= the entries counted
         const u32 hl = hm ? (u32)__builtin_ctzll(hm) : (u32)kWave - 1u;
         const u32 above = __builtin_amdgcn_readlane(incl - s, hl);
-        const u32 ci = l < 32u ? hist[kBins - 1u - 32u * hl - l] : 0u;
+        const u32 ci = l < kPerLane ? hist[kNB - 1u - kPerLane * hl - l] : 0u;
         const u32 in2 = wave_incl_scan(ci);
         const u64 jm = __ballot(above + in2 >= r);
-        const u32 jl = jm ? (u32)__builtin_ctzll(jm) : 31u;
+        const u32 jl = jm ? (u32)__builtin_ctzll(jm) : kPerLane - 1u;
         const u32 cc = __builtin_amdgcn_readlane(ci, jl);
         const u32 rr = r - (above + __builtin_amdgcn_readlane(in2, jl) - cc);
-        P |= (u64)(kBins - 1u - 32u * hl - jl) << sh;
+        P |= (u64)(kNB - 1u - kPerLane * hl - jl) << sh;
         if (rr >= cc || sh == 0) break;  // the whole sub-bin is kept: exactly k at or above P
         r = rr;
-        fixed = sh;
+        // The next window starts at the highest bit below sh where the
+        // sub-bin's entries (two or more: rr < cc) differ; the bits above it
+        // are the same in all of them.
+        const u64 pm2 = ~low_mask(sh);
+        u64 o = 0, a = ~0ull;
+#pragma unroll
+        for (u32 j = 0; j < (u32)kSmallJ; ++j)
+            if (j < jn && comp[j] != 0 && (comp[j] & pm2) == P) {
+                o |= comp[j];
+                a &= comp[j];
+            }
+        const u64 O = ((u64)wave_or((u32)(o >> 32)) << 32) | wave_or((u32)o);
+        const u64 A = ((u64)wave_and((u32)(a >> 32)) << 32) | wave_and((u32)a);
+        const u64 D = (O ^ A) & low_mask(sh);
+        const int hb = D ? 63 - __clzll((long long)D) : 0;
+        P |= A & low_mask(sh) & ~low_mask(hb + 1);
+        fixed = hb + 1;
     }
     const u64 T = P;
 
@@ -2742,7 +2772,7 @@ __global__ __launch_bounds__(kSmallWG) void topk_small_rows(Params p, int64_t ro
         const bool keep = j < jn && comp[j] >= T && comp[j] != 0;
         const u64 m = __ballot(keep);
         const u32 pos = run + mbcnt(m);
-        if (keep && pos < (u32)kSmallValueMax) list[pos] = ~comp[j];
+        if (keep && pos < kWords / 2u) list[pos] = ~comp[j];
         run += (u32)__popcll(m);
     }
     u32 Pn = 1;

@@ -21,7 +21,7 @@ def pkg():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 500, 2048])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 128, 255, 256, 257, 500, 2048])
 @pytest.mark.parametrize("levels", [0, 5])
 def test_short_rows_parity(pkg, oracle_mod, dtype, n, levels):
     raw = make_edge_rows(dtype, 9, n, seed=n * 3 + levels, levels=levels, specials=0.04)
