@@ -248,7 +248,10 @@ int ds_topk_ex(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_
  * The weights and sums are fp32: a draw within a few fp32 ulps of a
  * boundary may land on the neighbouring candidate of the exact (real
  * number) draw.  The library keeps the k candidates of each row in a
- * per-(device, stream) buffer of its own.
+ * per-(device, stream) buffer of its own.  For rows of more than 2048
+ * columns with k <= 1024 the workgroup that writes a row's value-ordered
+ * top-k also draws its token, in the same launch; otherwise a second kernel
+ * draws from the candidates.  Both follow the definition above in fp32.
  */
 int ds_topk_sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k,
                    const float* temperature, const float* top_p, const float* uniform, int32_t* out_token,

@@ -13,7 +13,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ds_topk.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
+# the selection with its sampling step, compiled as a unit of its own
+SAMPLE_SRC = os.path.join(HERE, "csrc", "sample_fused.hip")
+DEPS = [SRC, SAMPLE_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
         os.path.join(ROOT, "include", "ds_topk.h")]
 LIB = os.path.join(HERE, "libds_topk.so")
 # Measurement build of the same sources: the kernels also note phase
@@ -25,8 +27,8 @@ CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Files whose content decides the top-k kernels' code (for tagging profiles).
-KERNEL_SOURCES = (SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(ROOT, "include", "ds_topk.h"),
-                  os.path.abspath(__file__))
+KERNEL_SOURCES = (SRC, SAMPLE_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"),
+                  os.path.join(ROOT, "include", "ds_topk.h"), os.path.abspath(__file__))
 
 
 def kernel_source_sha() -> str:
@@ -62,10 +64,11 @@ def stale(lib: str = LIB, deps=None) -> bool:
     return any(os.path.getmtime(d) > t for d in deps)
 
 
-def _hipcc(src: str, lib: str, verbose: bool, extra=()) -> None:
+def _hipcc(src, lib: str, verbose: bool, extra=()) -> None:
     tmp = lib + ".tmp%d" % os.getpid()
+    srcs = [src] if isinstance(src, str) else list(src)
     cmd = [HIPCC] + FLAGS + list(extra) + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                                           "-o", tmp, src]
+                                           "-o", tmp] + srcs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:
@@ -80,11 +83,11 @@ def build(force: bool = True, verbose: bool = False, timing: bool = True) -> str
     calibration kernels) and, with `timing`, libds_topk_timing.so (the
     library with phase timestamps, for measurement only)."""
     if force or stale():
-        _hipcc(SRC, LIB, verbose)
+        _hipcc([SRC, SAMPLE_SRC], LIB, verbose)
     if force or stale(CALIB_LIB, [CALIB_SRC]):
         _hipcc(CALIB_SRC, CALIB_LIB, verbose)
     if timing and (force or stale(TIMING_LIB)):
-        _hipcc(SRC, TIMING_LIB, verbose, ["-DDSTK_TIMING"])
+        _hipcc([SRC, SAMPLE_SRC], TIMING_LIB, verbose, ["-DDSTK_TIMING"])
     return LIB
 
 

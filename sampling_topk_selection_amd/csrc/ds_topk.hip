@@ -25,20 +25,7 @@ constexpr int kMaxSegs = 256;       // workgroups per row (merge keeps one LDS c
 constexpr int kTargetWG = 256;      // one workgroup per CU on a 256-CU MI355X
 constexpr int kSegPerK = 8;         // a segment holds at least 8k columns
 constexpr int64_t kMinSegElems = 8192;  // and at least this many: below it the merge costs more than it saves
-// Tiles per chunk (16-byte loads in flight per thread and buffer), per
-// element width: a bf16 tile holds twice the elements of an fp32 one, and
-// its eight slots per vector take more registers to filter.
-#ifndef DS_TOPK_TILES_PER_CHUNK_F32
-#define DS_TOPK_TILES_PER_CHUNK_F32 4
-#endif
-#ifndef DS_TOPK_TILES_PER_CHUNK_BF16
-#define DS_TOPK_TILES_PER_CHUNK_BF16 2
-#endif
-// bf16 with k > 1024 (the larger buffer): one more tile in flight pays
-// there (measured), while it slows the smaller-k shapes
-#ifndef DS_TOPK_TILES_PER_CHUNK_BF16_BIGK
-#define DS_TOPK_TILES_PER_CHUNK_BF16_BIGK 3
-#endif
+// (tiles per chunk of each instance: DS_TOPK_TILES_PER_CHUNK_*, topk_kernels.hpp)
 constexpr int kChunkF32 = DS_TOPK_TILES_PER_CHUNK_F32;
 constexpr int kChunkBf16 = DS_TOPK_TILES_PER_CHUNK_BF16;
 constexpr int kChunkBf16BigK = DS_TOPK_TILES_PER_CHUNK_BF16_BIGK;
@@ -155,6 +142,14 @@ constexpr int64_t kSmallRows = dstk::kSmallWG / dstk::kWave;  // rows per workgr
 bool use_small(int64_t n, int32_t k, int sorted_index) {
     return n <= dstk::kSmallN && g_force_segs == 0 &&
            !(sorted_index == DS_ORDER_VALUE && k > dstk::kSmallValueMax);
+}
+
+// ds_topk_sample draws each row's token in the selection's own launch
+// (dstk::topk_sample_rows, after the row's value-ordered output) for the
+// workgroup-per-row kernels with k <= 1024; else a second kernel does it
+// (dssample::sample_rows) from the selection's output.
+bool sampling_fused(int64_t n, int32_t k, const Plan& pl) {
+    return !use_small(n, k, DS_ORDER_VALUE) && pl.cap == 8192;
 }
 
 // ------------------------------------------------------------------ workspace
@@ -286,12 +281,21 @@ hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
     hipLaunchKernelGGL((dstk::topk_rows<EB, WG, NV, CAP>), dim3((uint32_t)grid), dim3(WG), 0, s, prm);
     return hipGetLastError();
 }
+}  // namespace
+
+// The selection with its sampling step (sample_fused.hip: a translation unit
+// of its own, so the selection kernels here share no out-of-line function
+// with it and keep their own register allocation).
+hipError_t ds_topk_launch_sample_fused(int eb, const dstk::Params& prm, int64_t grid, hipStream_t s);
+
+namespace {
 
 // The instances make_plan can choose (element bytes, capacity).  (The
 // fp32 instances come first in the code object: the sampler kernel's
 // timing was measured in that placement.)
-hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s) {
+hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s, bool sample = false) {
     const int64_t grid = rows * pl.segs;
+    if (sample) return ds_topk_launch_sample_fused(pl.eb, prm, grid, s);  // (sampling_fused: capacity 8192)
     if (pl.eb == 4) {
         if (pl.cap == 8192) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
         return launch_one<4, 512, kChunkF32, 16384>(prm, grid, s);
@@ -300,11 +304,22 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
     return launch_one<2, 512, kChunkBf16BigK, 16384>(prm, grid, s);
 }
 
+// Per-row sampling inputs and the token output, for a selection that draws
+// the token in the same launch (see sampling_fused).
+struct SampleIn {
+    const float* temperature;
+    const float* top_p;
+    const float* uniform;
+    int32_t* out_token;
+};
+
 // Checks the arguments and enqueues the selection on `stream`; a NaN makes
-// the kernels store flag_value into *flag.
+// the kernels store flag_value into *flag.  With `samp` (value order, a plan
+// sampling_fused accepts) each row's workgroup also draws its token.
 int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stride, int32_t k, int sorted_index,
             int return_value, void* out_idx, void* out_val, const WsPtrs& ws, int32_t* flag, int32_t flag_value,
-            hipStream_t stream, const int32_t* lengths, int index_bytes, const Plan& pl) {
+            hipStream_t stream, const int32_t* lengths, int index_bytes, const Plan& pl,
+            const SampleIn* samp = nullptr) {
     const bool small = use_small(n, k, sorted_index);
     const int64_t es = dtype == DS_DTYPE_BF16 ? 2 : 4;
     for (int64_t r0 = 0; r0 < batch; r0 += pl.rows_per_launch) {
@@ -331,6 +346,12 @@ int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_str
         prm.flag_value = flag_value;
         prm.flags = (g_flags & dstk::kFlagBitonic) | (index_bytes == 8 ? dstk::kFlagIdx64 : 0);
         prm.lengths = lengths ? lengths + r0 : nullptr;
+        if (samp) {
+            prm.temperature = samp->temperature + r0;
+            prm.top_p = samp->top_p + r0;
+            prm.uniform = samp->uniform + r0;
+            prm.out_token = samp->out_token + r0;
+        }
 #ifdef DSTK_TIMING
         prm.timing = g_timing;
 #endif
@@ -352,7 +373,7 @@ int enqueue(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_str
                                    dim3(dstk::kSmallWG), 0, stream, prm, rows);
             e = hipGetLastError();
         } else {
-            e = launch(pl, prm, rows, stream);
+            e = launch(pl, prm, rows, stream, samp != nullptr);
         }
         if (e != hipSuccess) return hip_fail(e, "kernel launch");
     }
@@ -521,17 +542,21 @@ int sample(const void* in, int dtype, int64_t batch, int64_t n, int64_t row_stri
     if (st) return st;
     st = ensure(ws, pl.rows_per_launch, use_small(n, k, DS_ORDER_VALUE) ? 1 : pl.segs, pl.pub_cap, stream);
     if (st) return st;
+    const SampleIn samp{temperature, top_p, uniform, out_token};
+    const bool fused = sampling_fused(n, k, pl);
     st = enqueue(in, dtype, batch, n, row_stride, k, DS_ORDER_VALUE, 1, cidx, cval, ws->ptrs, ws->nan_word,
-                 DS_ERR_NAN, stream, nullptr, 4, pl);
+                 DS_ERR_NAN, stream, nullptr, 4, pl, fused ? &samp : nullptr);
     if (st) return st;
-    if (dtype == DS_DTYPE_BF16)
-        hipLaunchKernelGGL(dssample::sample_rows<uint16_t>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
-                           (const uint16_t*)cval, cidx, k, temperature, top_p, uniform, out_token);
-    else
-        hipLaunchKernelGGL(dssample::sample_rows<float>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
-                           (const float*)cval, cidx, k, temperature, top_p, uniform, out_token);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "sample launch");
+    if (!fused) {
+        if (dtype == DS_DTYPE_BF16)
+            hipLaunchKernelGGL(dssample::sample_rows<uint16_t>, dim3((uint32_t)batch), dim3(dssample::kWG), 0,
+                               stream, (const uint16_t*)cval, cidx, k, temperature, top_p, uniform, out_token);
+        else
+            hipLaunchKernelGGL(dssample::sample_rows<float>, dim3((uint32_t)batch), dim3(dssample::kWG), 0, stream,
+                               (const float*)cval, cidx, k, temperature, top_p, uniform, out_token);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "sample launch");
+    }
     return signal_and_wait(ws, next_epoch(ws), stream);
 }
 

@@ -40,6 +40,21 @@
 
 #include <type_traits>
 
+// Tiles per chunk (16-byte loads in flight per thread and buffer), per
+// element width: a bf16 tile holds twice the elements of an fp32 one, and
+// its eight slots per vector take more registers to filter.
+#ifndef DS_TOPK_TILES_PER_CHUNK_F32
+#define DS_TOPK_TILES_PER_CHUNK_F32 4
+#endif
+#ifndef DS_TOPK_TILES_PER_CHUNK_BF16
+#define DS_TOPK_TILES_PER_CHUNK_BF16 2
+#endif
+// bf16 with k > 1024 (the larger buffer): one more tile in flight pays
+// there (measured), while it slows the smaller-k shapes
+#ifndef DS_TOPK_TILES_PER_CHUNK_BF16_BIGK
+#define DS_TOPK_TILES_PER_CHUNK_BF16_BIGK 3
+#endif
+
 namespace dstk {
 
 using u32 = uint32_t;
@@ -233,6 +248,8 @@ struct Smem {
     u32 tie_col;           // seed: column of the tied k-th entry
     u32 tie_cnt[8];        // seed: the crowded bin's entries per bound tile
     u32 pubseed;           // split row: the histogram holds the seed's publishing offsets
+    u32 smp_m, smp_pick;   // sampling: nucleus end and the drawn slot
+    float smp_w;           // sampling: the nucleus weight
     u32 lwsum[16];       // block_locate: per-wave bin totals
     u32 lwfirst[16];     // block_locate: per-wave highest non-empty bin (waves with any)
     u64 trash[64];       // scan: written by the lanes that append nothing
@@ -1715,6 +1732,12 @@ struct Params {
     int32_t flags;     // kFlag* bits
     const int32_t* lengths;  // [batch] valid columns per row (clamped to [0, n]), or null: all n
     u64* timing;       // measurement build: [grid][kTimingSlots] phase timestamps; else unused
+    // the sampling instance (topk_sample_rows) only: per row temperature,
+    // top-p and a uniform, and the token drawn
+    const float* temperature;
+    const float* top_p;
+    const float* uniform;
+    int32_t* out_token;
 };
 
 // Output slots [k, kout) of a row with only k = len < kout valid columns:
@@ -1960,10 +1983,116 @@ __device__ __noinline__ SeedBound crowded_seed_bound(Smem<CAP>& sm, const uint8_
 // Exact selection of the k largest of buf[0, cnt) (bin b1 holds the k-th,
 // rank r1 of c1 inside it) and output, the −inf tail up to kout, then the
 // NaN report; the workgroup ends here.
+// ------------------------------------------------------------------ sampling
+// A row's sampling inputs and token output (the sampling instance).
+struct SampleIO {
+    const float* temperature;
+    const float* top_p;
+    const float* uniform;
+    int32_t* out_token;
+    u32 row;
+};
+
+// Inclusive prefix sum of floats across the 64 lanes (all lanes active).
+__device__ __forceinline__ float wave_incl_scan_f(float x) {
+    auto step = [&](auto ctrl, auto rmask) __attribute__((always_inline)) {
+        const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                  decltype(rmask)::value, 0xF, decltype(rmask)::value == 0xF);
+        x += __int_as_float(y);
+    };
+    step(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xF>{});  // row_shr:1
+    step(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xF>{});  // row_shr:2
+    step(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xF>{});  // row_shr:4
+    step(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xF>{});  // row_shr:8
+    step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15
+    step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31
+    return x;
+}
+
+// One token from the row's top-k, by the definition the sampling kernel
+// follows (sample_kernels.hpp): softmax weights at temperature T relative to
+// the largest value, the top-p nucleus as the shortest prefix reaching top_p
+// of the total weight, and the inverse CDF at the caller's uniform; T <= 0 is
+// greedy.  buf[0, k) holds the top-k in value order, the composites or,
+// when `cpl`, their complements (as the output step left them).  Call from
+// every thread after a barrier that follows the output.
 template <class E, int WG, int CAP>
+__device__ __forceinline__ void sample_sorted(Smem<CAP>& sm, u32 k, bool cpl, const SampleIO& io) {
+    constexpr u32 kMaxPer = 4096 / WG;  // candidates per thread (k <= 4096)
+    const u32 tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    auto comp_at = [&](u32 j) -> u64 { return cpl ? ~sm.buf[j] : sm.buf[j]; };
+    auto value = [&](u64 c) -> float {
+        const u32 b = E::bits(comp_key<E>(c));
+        return __uint_as_float(E::kKeyBits == 16 ? b << 16 : b);
+    };
+    const float T = io.temperature[io.row];
+    if (!(T > 0.0f)) {  // greedy (also for NaN)
+        if (tid == 0) io.out_token[io.row] = (int32_t)comp_col<E>(comp_at(0));
+        return;
+    }
+    const float invT = 1.0f / T;
+    const float x1 = value(comp_at(0));
+    const u32 per = (k + WG - 1) / WG;
+    const u32 j0 = tid * per;
+    float W[kMaxPer];
+    float run = 0.0f;
+#pragma unroll
+    for (u32 i = 0; i < kMaxPer; ++i) {
+        float w = 0.0f;
+        if (i < per && j0 + i < k) {
+            const float x = value(comp_at(j0 + i));
+            w = x == x1 ? 1.0f : (x == -__builtin_huge_valf() ? 0.0f : expf((x - x1) * invT));
+        }
+        run += w;
+        W[i] = run;
+    }
+    const float incl = wave_incl_scan_f(run);
+    float* const wsum = (float*)sm.wsum;
+    if (lane == kWave - 1) wsum[wave] = incl;
+    if (tid == 0) {
+        sm.smp_m = k - 1u;
+        sm.smp_pick = ~0u;
+    }
+    __syncthreads();
+    float base = incl - run, total = 0.0f;
+#pragma unroll
+    for (u32 q = 0; q < (u32)(WG / kWave); ++q) {
+        base += q < wave ? wsum[q] : 0.0f;
+        total += wsum[q];
+    }
+    const float thresh = io.top_p[io.row] * total;  // the nucleus: first j with W_j >= top_p W_k
+#pragma unroll
+    for (u32 i = 0; i < kMaxPer; ++i)
+        if (i < per && j0 + i < k && base + W[i] >= thresh) {
+            atomicMin(&sm.smp_m, j0 + i);
+            break;
+        }
+    __syncthreads();
+    const u32 m = sm.smp_m;
+    if (m >= j0 && m < j0 + per) sm.smp_w = base + W[m - j0];
+    __syncthreads();
+    float u = io.uniform[io.row];
+    if (!(u >= 0.0f)) u = 0.0f;
+    if (u >= 1.0f) u = 0x1.fffffep-1f;  // the largest float below 1
+    const float t = u * sm.smp_w;
+#pragma unroll
+    for (u32 i = 0; i < kMaxPer; ++i)
+        if (i < per && j0 + i <= m && base + W[i] > t) {
+            atomicMin(&sm.smp_pick, j0 + i);
+            break;
+        }
+    __syncthreads();
+    if (tid == 0) {
+        const u32 pk = sm.smp_pick <= m ? sm.smp_pick : m;
+        io.out_token[io.row] = (int32_t)comp_col<E>(comp_at(pk));
+    }
+}
+
+template <class E, int WG, int CAP, bool kSample = false>
 __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
                                              int sorted, int retval, int flags, gptr<void> row_idx_p, gptr<void> row_val,
-                                             gptr<int32_t> flag, int32_t flag_value, u64* timing) {
+                                             gptr<int32_t> flag, int32_t flag_value, u64* timing,
+                                             const SampleIO& sio = SampleIO{}) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
     const u32 cb = n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u;  // column bits
     const u64 T = refine<WG, CAP, E::kKeyBits == 32 ? 1 : 2>(sm, cnt, b1, r1, c1, cb);
@@ -1971,6 +2100,7 @@ __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, 
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
     __syncthreads();
+    if constexpr (kSample) sample_sorted<E, WG, CAP>(sm, k, k > (u32)WG, sio);
     if (threadIdx.x == 0 && sm.nan) *flag = flag_value;
     DSTK_T(sm, kPhEmit);
     DSTK_T_FLUSH(sm, timing);
@@ -2048,9 +2178,15 @@ __device__ __noinline__ void merge_fallback(Smem<CAP>& sm, gptr<const u64> rmeta
 // candidate-buffer entries.
 // A "tile" is one vector per thread, WG * 16 bytes; tiles are visited in a
 // pseudo-random order, a chunk at a time.
-template <int EB, int WG, int NV, int CAP>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WG / 256)))
-void topk_rows(Params p) {
+// The sampling inputs of a row (only the sampling instance reads them).
+template <bool kSample>
+__device__ __forceinline__ SampleIO sample_io(const Params& p, u32 row) {
+    if constexpr (kSample) return SampleIO{p.temperature, p.top_p, p.uniform, p.out_token, row};
+    return SampleIO{};
+}
+
+template <int EB, int WG, int NV, int CAP, bool kSample>
+__device__ __forceinline__ void topk_rows_body(const Params& p) {
     using E = Elem<EB>;
     using SL = Slot<E, 1, WG>;
     constexpr int kTileVecs = WG;
@@ -2373,8 +2509,9 @@ void topk_rows(Params p) {
     if (S == 1) {
         block_locate<WG, CAP>(sm, k, 0u, true);
         DSTK_T(sm, kPhLocate);
-        select_and_emit<E, WG, CAP>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, kout, n, sorted,
-                                    retval, flags, row_idx.p, row_val, flag, flag_value, timing);
+        select_and_emit<E, WG, CAP, kSample>(sm, cnt, sm.loc_digit[0], sm.loc_r[0], sm.loc_c[0], k, kout, n, sorted,
+                                             retval, flags, row_idx.p, row_val, flag, flag_value, timing,
+                                             sample_io<kSample>(p, row));
         return;
     }
 
@@ -2587,6 +2724,10 @@ void topk_rows(Params p) {
                                    sorted, retval,
                                    flags, row_idx.p, row_val, flag, flag_value);
         if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
+        if constexpr (kSample) {
+            __syncthreads();
+            sample_sorted<E, WG, CAP>(sm, k, k > (u32)WG, sample_io<kSample>(p, row));
+        }
         DSTK_T(sm, kPhEmit);
         DSTK_T_FLUSH(sm, timing);
         return;
@@ -2618,8 +2759,22 @@ void topk_rows(Params p) {
     }
     __syncthreads();
     DSTK_T(sm, kPhMergeLocate);
-    select_and_emit<E, WG, CAP>(sm, total, b1, r1, c1, k, kout, n, sorted, retval, flags, row_idx.p, row_val,
-                                flag, flag_value, timing);
+    select_and_emit<E, WG, CAP, kSample>(sm, total, b1, r1, c1, k, kout, n, sorted, retval, flags, row_idx.p, row_val,
+                                         flag, flag_value, timing,
+                                         sample_io<kSample>(p, row));
+}
+
+// The selection kernel, and the same with the sampling step after a row's
+// value-ordered output (one token per row: ds_topk_sample in one launch).
+template <int EB, int WG, int NV, int CAP>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WG / 256)))
+void topk_rows(Params p) {
+    topk_rows_body<EB, WG, NV, CAP, false>(p);
+}
+template <int EB, int WG, int NV, int CAP>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(WG / 256)))
+void topk_sample_rows(Params p) {
+    topk_rows_body<EB, WG, NV, CAP, true>(p);
 }
 
 }  // namespace dstk

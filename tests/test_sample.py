@@ -95,6 +95,30 @@ def test_sample_edges(pkg, oracle_mod, dtype):
     _check(pkg, oracle_mod, raw, dtype, n, k, T, P, U)
 
 
+@pytest.mark.parametrize("dtype,n,k,segs,levels", [
+    ("f32", 1500, 100, 0, 0),     # one wave per row, then the sampling kernel
+    ("bf16", 40000, 2000, 0, 0),  # k > 1024: the sampling kernel after the selection
+    ("f32", 20000, 700, 0, 7),    # drawn in the selection's launch, k above one entry per thread
+    ("bf16", 9000, 1024, 0, 0),   # the largest k drawn in the selection's launch
+    ("bf16", 60000, 300, 3, 0),   # split rows: the merging workgroup draws
+    ("f32", 60000, 700, 4, 5),    # split rows, k above one entry per thread
+])
+def test_sample_paths(pkg, oracle_mod, dtype, n, k, segs, levels):
+    B = 6
+    raw = make_edge_rows(dtype, B, n, seed=n + k, levels=levels, specials=0.0)
+    rng = np.random.default_rng(n * 7 + k)
+    T = rng.uniform(0.2, 3.0, B).astype(np.float32)
+    T[0] = 0.0  # greedy
+    P = rng.uniform(0.3, 1.0, B).astype(np.float32)
+    U = rng.random(B).astype(np.float32)
+    log("sample path %s n=%d k=%d segs=%d levels=%d" % (dtype, n, k, segs, levels))
+    pkg.ds_topk_set_overrides(segs, 0, 0)
+    try:
+        _check(pkg, oracle_mod, raw, dtype, n, k, T, P, U)
+    finally:
+        pkg.ds_topk_set_overrides(0, 0, 0)
+
+
 def test_sample_nan_is_reported(pkg):
     import torch
 
