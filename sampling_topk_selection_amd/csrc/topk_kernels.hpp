@@ -248,6 +248,7 @@ struct Smem {
     u32 tie_col;           // seed: column of the tied k-th entry
     u32 tie_cnt[8];        // seed: the crowded bin's entries per bound tile
     u32 pubseed;           // split row: the histogram holds the seed's publishing offsets
+    u64 chain_t;           // refine: the k-th composite found by a chain walk
     u32 smp_m, smp_pick;   // sampling: nucleus end and the drawn slot
     float smp_w;           // sampling: the nucleus weight
     u32 lwsum[16];       // block_locate: per-wave bin totals
@@ -1153,6 +1154,33 @@ __device__ __forceinline__ u64 side_select(Smem<CAP>& sm, u32 cnt, u64 mask, u64
            (u32)__builtin_amdgcn_readlane((u32)x, hl);
 }
 
+// The rr-th largest of the c entries of a first-level sub-bin, found by
+// walking the sub-bin's chain: head[d] is the last of its entries to be
+// counted, next[i] the one counted before entry i (the first one's link is
+// never followed).  One lane walks it into sm.trash, the wave ranks the c
+// entries (a wave's LDS accesses take effect in order); the result is
+// shared through LDS.  Call from every thread.
+template <int WG, int CAP>
+__device__ __forceinline__ u64 chain_select(Smem<CAP>& sm, const u32* head, const u32* next, u32 d, u32 c, u32 rr) {
+    const u32 l = lane_id();
+    if (threadIdx.x < (u32)kWave) {
+        if (l == 0) {
+            u32 i = head[d];
+            for (u32 j = 0; j < c; ++j) {
+                sm.trash[j] = sm.buf[i];
+                if (j + 1 < c) i = next[i];
+            }
+        }
+        const u64 x = l < c ? sm.trash[l] : 0ull;
+        u32 above = 0;
+        for (u32 q = 0; q < c; ++q) above += sm.trash[q] > x ? 1u : 0u;
+        const u64 hit = __ballot(l < c && above == rr - 1);  // one lane: the entries are distinct
+        if (hit && l == (u32)__builtin_ctzll(hit)) sm.chain_t = x;
+    }
+    __syncthreads();
+    return sm.chain_t;
+}
+
 // A sub-bin this small is settled by side_select rather than another radix
 // level (measured: with more entries, the gather and the ranking cost more
 // than a level).
@@ -1190,15 +1218,28 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
     // kFirst 2: the column part's length and position
     const u32 len2 = cb < 6u ? cb : 6u;
     const int csh = 16 + (int)cb - (int)len2;
+    // With a fixed first level, the entries of each of its sub-bins are also
+    // chained (heads and links in the free buffer behind the entries, when
+    // they fit), so a small sub-bin holding the k-th is ranked by one wave
+    // without another pass (chain_select).  Not in the k > 1024 kernels:
+    // there the k-th entry's bin can hold thousands of tied entries, whose
+    // returning atomics cost more than the pass they save (256 x 32768,
+    // k = 4096, 16 levels: +1.4 us).
+    const bool chain = kFirst != 0 && CAP == 8192 && (u64)cnt * 12u + (u64)kBins * 4u <= (u64)CAP * 8u;
+    u32* const head = (u32*)(sm.buf + cnt);
+    u32* const next = head + kBins;
     for (u32 i = tid; i < cnt; i += WG) {
         const u64 e = sm.buf[i];
         if (top_digit(e) == b1) {
             o |= e;
             a &= e;
-            if constexpr (kFirst == 1) atomicAdd(&sm.hist[hidx((u32)(e >> kSh1) & (kBins - 1))], 1u);
-            if constexpr (kFirst == 2)
-                atomicAdd(&sm.hist[hidx((((u32)(e >> 48) & 31u) << len2) | ((u32)(e >> csh) & ((1u << len2) - 1u)))],
-                          1u);
+            u32 d = 0;
+            if constexpr (kFirst == 1) d = (u32)(e >> kSh1) & (kBins - 1);
+            if constexpr (kFirst == 2) d = (((u32)(e >> 48) & 31u) << len2) | ((u32)(e >> csh) & ((1u << len2) - 1u));
+            if constexpr (kFirst != 0) {
+                atomicAdd(&sm.hist[hidx(d)], 1u);
+                if (chain) next[i] = atomicExch(&head[d], i);
+            }
         }
     }
     if constexpr (kFirst == 1) {
@@ -1208,7 +1249,10 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         fixed = kSh1;
         r = sm.loc_r[0];
         if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
-        if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(kSh1), P, r);
+        if (sm.loc_c[0] <= kSideMax) {
+            if (chain) return chain_select<WG, CAP>(sm, head, next, sm.loc_digit[0], sm.loc_c[0], r);
+            return side_select<WG, CAP>(sm, cnt, ~low_mask(kSh1), P, r);
+        }
     }
     if constexpr (kFirst == 2) {
         __syncthreads();
@@ -1219,7 +1263,10 @@ __device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u3
         fixed = csh;
         r = sm.loc_r[0];
         if (r >= sm.loc_c[0]) return P;  // the whole sub-bin is kept: T is its least possible key
-        if (sm.loc_c[0] <= kSideMax) return side_select<WG, CAP>(sm, cnt, ~low_mask(csh), P, r);
+        if (sm.loc_c[0] <= kSideMax) {
+            if (chain) return chain_select<WG, CAP>(sm, head, next, d, sm.loc_c[0], r);
+            return side_select<WG, CAP>(sm, cnt, ~low_mask(csh), P, r);
+        }
     }
     {
         const u32 ohi = wave_or((u32)(o >> 32)), olo = wave_or((u32)o);
