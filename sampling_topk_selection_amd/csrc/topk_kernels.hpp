@@ -1204,42 +1204,76 @@ constexpr u32 kSideMax = 16;
 // 16-bit keys the first digit already takes high column bits below the
 // value's, so a tied value's entries spread over many sub-bins).  The
 // histogram must be zero on entry and is zero again on return.
-template <int WG, int CAP, int kFirst = 0>
-__device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 cb = 0) {
-    if (r1 >= c1) return digit_floor(b1);  // the whole bin is kept
+// The fixed first refine level (kFirst 1: 32-bit keys, kFirst 2: 16-bit
+// keys; see refine) for buf[0, cnt): an entry of the k-th entry's bin is
+// counted by its digit, gathered into the OR / AND of the bin, and chained
+// into its sub-bin.  With a fixed first level, the entries of each sub-bin
+// are chained (heads and links in the free buffer behind the entries, when
+// they fit), so a small sub-bin holding the k-th is ranked by one wave
+// without another pass (chain_select).  Not in the k > 1024 kernels: there
+// the k-th entry's bin can hold thousands of tied entries, whose returning
+// atomics cost more than the pass they save (256 x 32768, k = 4096, 16
+// levels: +1.4 us).
+template <int kFirst, int CAP>
+struct FirstLevel {
+    static constexpr int kSh1 = 64 - 2 * kHistBits;
+    u32 len2;  // kFirst 2: the column part's length and position
+    int csh;
+    bool chain;
+    u32* head;
+    u32* next;
+    __device__ __forceinline__ FirstLevel(Smem<CAP>& sm, u32 cnt, u32 cb)
+        : len2(cb < 6u ? cb : 6u), csh(16 + (int)cb - (int)(cb < 6u ? cb : 6u)),
+          chain(kFirst != 0 && CAP == 8192 && (u64)cnt * 12u + (u64)kBins * 4u <= (u64)CAP * 8u),
+          head((u32*)(sm.buf + cnt)), next((u32*)(sm.buf + cnt) + kBins) {}
+    __device__ __forceinline__ u32 digit(u64 e) const {
+        if constexpr (kFirst == 1) return (u32)(e >> kSh1) & (kBins - 1);
+        return (((u32)(e >> 48) & 31u) << len2) | ((u32)(e >> csh) & ((1u << len2) - 1u));
+    }
+    // entry i (= e) of the bin
+    __device__ __forceinline__ void add(Smem<CAP>& sm, u64 e, u32 i, u64& o, u64& a) const {
+        o |= e;
+        a &= e;
+        if constexpr (kFirst != 0) {
+            const u32 d = digit(e);
+            atomicAdd(&sm.hist[hidx(d)], 1u);
+            if (chain) next[i] = atomicExch(&head[d], i);
+        }
+    }
+};
+
+// kCounted: the caller has already passed every entry of bin b1 through
+// FirstLevel::add (the merge does it while loading), and o, a are its
+// thread's OR and AND.
+template <int WG, int CAP, int kFirst = 0, bool kCounted = false>
+__device__ __forceinline__ u64 refine(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 cb = 0, u64 o0 = 0,
+                                      u64 a0 = ~0ull) {
     const u32 tid = threadIdx.x, wave = tid / kWave;
+    if (r1 >= c1) {  // the whole bin is kept
+        if constexpr (kCounted) {
+            __syncthreads();
+            for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;
+            __syncthreads();
+        }
+        return digit_floor(b1);
+    }
     constexpr int kTop = 64 - kHistBits;
     constexpr int kSh1 = kTop - kHistBits;
     if (tid == 0) sm.side_count = 0;  // (read after the barriers below)
     u64 P = digit_floor(b1);  // bits of T fixed so far: those at or above `fixed`
     int fixed = kTop;
     u32 r = r1;
-    u64 o = 0, a = ~0ull;
-    // kFirst 2: the column part's length and position
-    const u32 len2 = cb < 6u ? cb : 6u;
-    const int csh = 16 + (int)cb - (int)len2;
-    // With a fixed first level, the entries of each of its sub-bins are also
-    // chained (heads and links in the free buffer behind the entries, when
-    // they fit), so a small sub-bin holding the k-th is ranked by one wave
-    // without another pass (chain_select).  Not in the k > 1024 kernels:
-    // there the k-th entry's bin can hold thousands of tied entries, whose
-    // returning atomics cost more than the pass they save (256 x 32768,
-    // k = 4096, 16 levels: +1.4 us).
-    const bool chain = kFirst != 0 && CAP == 8192 && (u64)cnt * 12u + (u64)kBins * 4u <= (u64)CAP * 8u;
-    u32* const head = (u32*)(sm.buf + cnt);
-    u32* const next = head + kBins;
-    for (u32 i = tid; i < cnt; i += WG) {
-        const u64 e = sm.buf[i];
-        if (top_digit(e) == b1) {
-            o |= e;
-            a &= e;
-            u32 d = 0;
-            if constexpr (kFirst == 1) d = (u32)(e >> kSh1) & (kBins - 1);
-            if constexpr (kFirst == 2) d = (((u32)(e >> 48) & 31u) << len2) | ((u32)(e >> csh) & ((1u << len2) - 1u));
-            if constexpr (kFirst != 0) {
-                atomicAdd(&sm.hist[hidx(d)], 1u);
-                if (chain) next[i] = atomicExch(&head[d], i);
-            }
+    u64 o = o0, a = a0;
+    const FirstLevel<kFirst, CAP> fl(sm, cnt, cb);
+    const u32 len2 = fl.len2;
+    const int csh = fl.csh;
+    const bool chain = fl.chain;
+    u32* const head = fl.head;
+    u32* const next = fl.next;
+    if constexpr (!kCounted) {
+        for (u32 i = tid; i < cnt; i += WG) {
+            const u64 e = sm.buf[i];
+            if (top_digit(e) == b1) fl.add(sm, e, i, o, a);
         }
     }
     if constexpr (kFirst == 1) {
@@ -2135,14 +2169,20 @@ __device__ __forceinline__ void sample_sorted(Smem<CAP>& sm, u32 k, bool cpl, co
     }
 }
 
-template <class E, int WG, int CAP, bool kSample = false>
+// The column bits of a row of n columns, and the fixed first refine level
+// of an element type.
+__device__ __forceinline__ u32 col_bits(u32 n) { return n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u; }
+template <class E>
+constexpr int kFirstOf = E::kKeyBits == 32 ? 1 : 2;
+
+template <class E, int WG, int CAP, bool kSample = false, bool kCounted = false>
 __device__ __forceinline__ void select_and_emit(Smem<CAP>& sm, u32 cnt, u32 b1, u32 r1, u32 c1, u32 k, u32 kout, u32 n,
                                              int sorted, int retval, int flags, gptr<void> row_idx_p, gptr<void> row_val,
                                              gptr<int32_t> flag, int32_t flag_value, u64* timing,
-                                             const SampleIO& sio = SampleIO{}) {
+                                             const SampleIO& sio = SampleIO{}, u64 o = 0, u64 a = ~0ull) {
     const IdxOut row_idx{row_idx_p, flags & kFlagIdx64};
-    const u32 cb = n > 1u ? 32u - (u32)__clz((int)(n - 1u)) : 0u;  // column bits
-    const u64 T = refine<WG, CAP, E::kKeyBits == 32 ? 1 : 2>(sm, cnt, b1, r1, c1, cb);
+    const u32 cb = col_bits(n);
+    const u64 T = refine<WG, CAP, kFirstOf<E>, kCounted>(sm, cnt, b1, r1, c1, cb, o, a);
     DSTK_T(sm, kPhRefine);
     emit_threshold<E, WG, CAP>(sm, cnt, T, k, n, sorted, retval, flags, row_idx, row_val);
     if (k < kout) write_tail<E, WG>(row_idx, row_val, k, kout);
@@ -2779,36 +2819,46 @@ __device__ __forceinline__ void topk_rows_body(const Params& p) {
         DSTK_T_FLUSH(sm, timing);
         return;
     }
+    // The shares are loaded, and the entries of the k-th entry's bin are
+    // counted for the refine's first level (and chained) as they arrive: no
+    // pass over the buffer afterwards.
+    u64 fo = 0, fa = ~0ull;  // OR / AND of this thread's entries of bin b1
     {
-        for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;  // zero for the selection
         // G threads per segment load its share (no search for the source)
         const u32 G = (u32)WG / S;  // (S <= 256: two or more)
         const u32 s_ = tid / G, j0 = tid - s_ * G;
-        if (s_ < S) {
-            const u32 off = sm.seg_count[s_];
-            const u32 share = (s_ + 1 < S ? sm.seg_count[s_ + 1] : total) - off;
-            const gptr<const u64> src = rc + (u64)s_ * cap;
-            constexpr int kLB = 4;  // loads in flight per thread
-            for (u32 j = j0; j < share; j += G * kLB) {
-                u64 v[kLB];
+        const u32 off = s_ < S ? sm.seg_count[s_] : 0u;
+        const u32 share = s_ < S ? (s_ + 1 < S ? sm.seg_count[s_ + 1] : total) - off : 0u;
+        const gptr<const u64> src = rc + (u64)(s_ < S ? s_ : 0u) * cap;
+        constexpr int kLB = 4;  // loads in flight per thread
+        u64 v[kLB];
+        auto load = [&](u32 j) __attribute__((always_inline)) {
 #pragma unroll
-                for (int u = 0; u < kLB; ++u) {
-                    const u32 jj = j + (u32)u * G;
-                    v[u] = jj < share ? ld_agent(&src[jj]) : 0ull;
-                }
+            for (int u = 0; u < kLB; ++u) {
+                const u32 jj = j + (u32)u * G;
+                v[u] = jj < share ? ld_agent(&src[jj]) : 0ull;
+            }
+        };
+        load(j0);  // (in flight while the histogram is cleared)
+        for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;  // zero for the selection
+        __syncthreads();
+        const FirstLevel<kFirstOf<E>, CAP> fl(sm, total, col_bits(n));
+        for (u32 j = j0; j < share; j += G * kLB) {
 #pragma unroll
-                for (int u = 0; u < kLB; ++u) {
-                    const u32 jj = j + (u32)u * G;
-                    if (jj < share) sm.buf[off + jj] = v[u];
+            for (int u = 0; u < kLB; ++u) {
+                const u32 jj = j + (u32)u * G;
+                if (jj < share) {
+                    sm.buf[off + jj] = v[u];
+                    if (top_digit(v[u]) == b1) fl.add(sm, v[u], off + jj, fo, fa);
                 }
             }
+            if (j + G * kLB < share) load(j + G * kLB);
         }
     }
     __syncthreads();
     DSTK_T(sm, kPhMergeLocate);
-    select_and_emit<E, WG, CAP, kSample>(sm, total, b1, r1, c1, k, kout, n, sorted, retval, flags, row_idx.p, row_val,
-                                         flag, flag_value, timing,
-                                         sample_io<kSample>(p, row));
+    select_and_emit<E, WG, CAP, kSample, true>(sm, total, b1, r1, c1, k, kout, n, sorted, retval, flags, row_idx.p,
+                                               row_val, flag, flag_value, timing, sample_io<kSample>(p, row), fo, fa);
 }
 
 // The selection kernel, and the same with the sampling step after a row's
