@@ -2714,99 +2714,183 @@ __device__ __forceinline__ void topk_rows_body(const Params& p) {
         return j < kDirCache ? dc[s_ * kDirCache + j] : ld_agent(&rdir[(u64)s_ * kBins + j]);
     };
     DSTK_T(sm, kPhHeaders);
-    // Row histogram of the published entries, from the directories: one
-    // thread per (segment, cached directory entry), then the entries of
-    // segments with more bins than the cache holds.
-    for (u32 i = tid; i < S * kDirCache; i += WG) {
-        const u32 s_ = i / kDirCache, j = i % kDirCache;
-        const u64 m0 = mc[s_ * 4];
-        const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
-        if (lv > 0 && j <= dh - dl) {
-            const u32 c = dc[i] - (j ? dc[i - 1] : 0u);
-            if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
-            if (j == 0) atomicMax(&sm.d_hi, dh);
+    // Each segment's list head is requested now, up to its published count
+    // (the share, a prefix of the list, is known only after the row bin), so
+    // the row bin is worked out while the loads are in flight.
+    const u32 G = (u32)WG / S;  // threads per segment in the list load (S <= 256: two or more)
+    const u32 ls = tid / G, lj0 = tid - ls * G;
+    const gptr<const u64> src = rc + (u64)(ls < S ? ls : 0u) * cap;
+    constexpr int kLB = 4;  // loads in flight per thread
+    u64 v[kLB];
+    auto load = [&](u32 j, u32 lim) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kLB; ++u) {
+            const u32 jj = j + (u32)u * G;
+            v[u] = jj < lim ? ld_agent(&src[jj]) : 0ull;
         }
-    }
+    };
     {
-        // Below the row bound (the largest segment bound, or the smallest
-        // q-bound if that is larger: either leaves k entries of the row at or
-        // above it) no bin is needed; it is worked out by a wave that meets
-        // such a segment.
-        u32 dL = 0;
-        bool have_dL = false;
-        for (u32 s_ = wave; s_ < S; s_ += WG / kWave) {
-            const u64 m0 = mc[s_ * 4];
-            const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
-            if (lv == 0 || dh - dl < kDirCache) continue;
-            if (!have_dL) {
-                u64 lmax = 0, qmin = ~0ull;
-                for (u32 t = lane_id(); t < S; t += kWave) {
-                    lmax = mc[t * 4 + 2] > lmax ? mc[t * 4 + 2] : lmax;
-                    qmin = mc[t * 4 + 3] < qmin ? mc[t * 4 + 3] : qmin;
-                }
-                lmax = wave_max64(lmax);
-                qmin = wave_min64(qmin);
-                dL = top_digit(lmax > qmin ? lmax : qmin);
-                have_dL = true;
-            }
-            const u32 lo = dl > dL ? dl : dL;
-            for (u32 j = kDirCache + lane_id(); dh >= lo && j <= dh - lo; j += kWave) {
-                const u32 c = dirv(s_, j) - dirv(s_, j - 1);
-                if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
-            }
-        }
+        const u32 lv = ls < S ? (u32)mc[ls * 4] : 0u;
+        load(lj0, lv < cap ? lv : cap);
     }
-    __syncthreads();
-    if (wave == 0) {
-        // One wave walks the bins down from the highest published one to
-        // the bin of the row's k-th entry (the counts at and above it are
-        // complete: every segment publishes all of its entries at or above
-        // its own k-th's bin, which lies at or below the row's), then gives
-        // each segment's share (its entries at or above that bin, a prefix
-        // of its list) and their offsets.
+    // With few segments, each directory within its cached head, every wave
+    // works out the row's k-th bin and the shares itself from the segments'
+    // cumulative counts (lane s holds segment s's metadata): no row histogram
+    // and no barrier before the list load.
+    constexpr u32 kDirectS = 16;
+    bool direct = false;
+    u32 lv_l = 0, dl_l = 0, dh_l = 0;
+    if (S <= kDirectS) {
+        if (lane_id() < S) {
+            const u64 m0 = mc[lane_id() * 4];
+            lv_l = (u32)m0;
+            dl_l = (u32)(m0 >> 32);
+            dh_l = (u32)mc[lane_id() * 4 + 1];
+        }
+        direct = __ballot(lv_l > 0 && dh_l - dl_l >= kDirCache) == 0;
+    }
+    u32 b1 = 0, r1 = 0, c1 = 0, total = 0, d_off = 0, d_share = 0;
+    if (direct) {
         const u32 l = lane_id();
-        const u32 dhm = __builtin_amdgcn_readfirstlane(sm.d_hi);  // highest published bin
-        // (the first 64 segments' metadata, read ahead of the walk)
-        const u64 m0a = l < S ? mc[l * 4] : 0ull;
-        const u32 dha = l < S ? (u32)mc[l * 4 + 1] : 0u;
-        u32 b1 = 0, r1 = 0, c1 = 0, above = 0;
+        const u32 dhm = wave_max(lv_l > 0 ? dh_l : 0u);  // highest published bin
+        // C(b): entries of the row published with top digit >= b, for this
+        // lane's bin b; the first bin (walking down) with C(b) >= k holds the
+        // k-th.
+        u32 prev = 0;  // C of the bin above the current 64
         for (u32 j0 = 0; j0 <= dhm; j0 += kWave) {
-            const u32 c = j0 + l <= dhm ? sm.hist[hidx(dhm - j0 - l)] : 0u;
-            const u32 incl = wave_incl_scan(c);
-            const u64 hit = __ballot(above + incl >= k);
+            const bool in = j0 + l <= dhm;
+            const u32 b = dhm - j0 - l;
+            u32 C = 0;
+            for (u32 s_ = 0; s_ < S; ++s_) {
+                const u32 lv = __builtin_amdgcn_readlane(lv_l, s_);
+                if (lv == 0) continue;
+                const u32 dl = __builtin_amdgcn_readlane(dl_l, s_), dh = __builtin_amdgcn_readlane(dh_l, s_);
+                const bool mid = b > dl && b <= dh;  // then dh - b < kDirCache
+                const u32 dv = dc[s_ * kDirCache + (mid ? dh - b : 0u)];
+                C += b > dh ? 0u : (mid ? dv : lv);
+            }
+            const u64 hit = __ballot(in && C >= k);
             if (hit) {
-                const u32 hl = hit ? (u32)__builtin_ctzll(hit) : 0u;
+                const u32 hl = (u32)__builtin_ctzll(hit);
+                const u32 ch = __builtin_amdgcn_readlane(C, hl);
+                const u32 cp = hl ? __builtin_amdgcn_readlane(C, hl - 1) : prev;
                 b1 = dhm - j0 - hl;
-                c1 = __builtin_amdgcn_readlane(c, hl);
-                r1 = k - (above + __builtin_amdgcn_readlane(incl, hl) - c1);
+                c1 = ch - cp;
+                r1 = k - cp;
                 break;
             }
-            above += __builtin_amdgcn_readlane(incl, kWave - 1);
+            prev = __builtin_amdgcn_readlane(C, kWave - 1);
         }
-        u32 carry = 0;
-        for (u32 s0 = 0; s0 < S; s0 += kWave) {
-            const u32 s_ = s0 + l;
-            u32 m = 0;
-            if (s_ < S) {
-                const u64 m0 = s0 ? mc[s_ * 4] : m0a;
-                const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = s0 ? (u32)mc[s_ * 4 + 1] : dha;
-                if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(s_, dh - b1);
+        // segment l's share: its entries at or above b1
+        const bool mid = lv_l > 0 && dh_l >= b1 && b1 > dl_l;
+        const u32 dv = dc[(l < S ? l : 0u) * kDirCache + (mid ? dh_l - b1 : 0u)];
+        const u32 m = lv_l > 0 && dh_l >= b1 ? (mid ? dv : lv_l) : 0u;
+        const u32 incl = wave_incl_scan(m);
+        total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        const u32 s_ = ls;
+        d_off = (u32)__builtin_amdgcn_ds_bpermute((int)((s_ & (kWave - 1)) * 4), (int)(incl - m));
+        d_share = (u32)__builtin_amdgcn_ds_bpermute((int)((s_ & (kWave - 1)) * 4), (int)m);
+        if (s_ >= S) d_share = 0;
+    } else {
+        // Row histogram of the published entries, from the directories: one
+        // thread per (segment, cached directory entry), then the entries of
+        // segments with more bins than the cache holds.
+        for (u32 i = tid; i < S * kDirCache; i += WG) {
+            const u32 s_ = i / kDirCache, j = i % kDirCache;
+            const u64 m0 = mc[s_ * 4];
+            const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+            if (lv > 0 && j <= dh - dl) {
+                const u32 c = dc[i] - (j ? dc[i - 1] : 0u);
+                if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
+                if (j == 0) atomicMax(&sm.d_hi, dh);
             }
-            const u32 incl = wave_incl_scan(m);
-            if (s_ < S) sm.seg_count[s_] = carry + incl - m;
-            carry += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
-        if (l == 0) {
-            sm.loc_digit[0] = b1;
-            sm.loc_r[0] = r1;
-            sm.loc_c[0] = c1;
-            sm.newtotal = carry;
+        {
+            // Below the row bound (the largest segment bound, or the smallest
+            // q-bound if that is larger: either leaves k entries of the row at or
+            // above it) no bin is needed; it is worked out by a wave that meets
+            // such a segment.
+            u32 dL = 0;
+            bool have_dL = false;
+            for (u32 s_ = wave; s_ < S; s_ += WG / kWave) {
+                const u64 m0 = mc[s_ * 4];
+                const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = (u32)mc[s_ * 4 + 1];
+                if (lv == 0 || dh - dl < kDirCache) continue;
+                if (!have_dL) {
+                    u64 lmax = 0, qmin = ~0ull;
+                    for (u32 t = lane_id(); t < S; t += kWave) {
+                        lmax = mc[t * 4 + 2] > lmax ? mc[t * 4 + 2] : lmax;
+                        qmin = mc[t * 4 + 3] < qmin ? mc[t * 4 + 3] : qmin;
+                    }
+                    lmax = wave_max64(lmax);
+                    qmin = wave_min64(qmin);
+                    dL = top_digit(lmax > qmin ? lmax : qmin);
+                    have_dL = true;
+                }
+                const u32 lo = dl > dL ? dl : dL;
+                for (u32 j = kDirCache + lane_id(); dh >= lo && j <= dh - lo; j += kWave) {
+                    const u32 c = dirv(s_, j) - dirv(s_, j - 1);
+                    if (c) atomicAdd(&sm.hist[hidx(dh - j)], c);
+                }
+            }
         }
+        __syncthreads();
+        if (wave == 0) {
+            // One wave walks the bins down from the highest published one to
+            // the bin of the row's k-th entry (the counts at and above it are
+            // complete: every segment publishes all of its entries at or above
+            // its own k-th's bin, which lies at or below the row's), then gives
+            // each segment's share (its entries at or above that bin, a prefix
+            // of its list) and their offsets.
+            const u32 l = lane_id();
+            const u32 dhm = __builtin_amdgcn_readfirstlane(sm.d_hi);  // highest published bin
+            // (the first 64 segments' metadata, read ahead of the walk)
+            const u64 m0a = l < S ? mc[l * 4] : 0ull;
+            const u32 dha = l < S ? (u32)mc[l * 4 + 1] : 0u;
+            u32 b1 = 0, r1 = 0, c1 = 0, above = 0;
+            for (u32 j0 = 0; j0 <= dhm; j0 += kWave) {
+                const u32 c = j0 + l <= dhm ? sm.hist[hidx(dhm - j0 - l)] : 0u;
+                const u32 incl = wave_incl_scan(c);
+                const u64 hit = __ballot(above + incl >= k);
+                if (hit) {
+                    const u32 hl = hit ? (u32)__builtin_ctzll(hit) : 0u;
+                    b1 = dhm - j0 - hl;
+                    c1 = __builtin_amdgcn_readlane(c, hl);
+                    r1 = k - (above + __builtin_amdgcn_readlane(incl, hl) - c1);
+                    break;
+                }
+                above += __builtin_amdgcn_readlane(incl, kWave - 1);
+            }
+            u32 carry = 0;
+            for (u32 s0 = 0; s0 < S; s0 += kWave) {
+                const u32 s_ = s0 + l;
+                u32 m = 0;
+                if (s_ < S) {
+                    const u64 m0 = s0 ? mc[s_ * 4] : m0a;
+                    const u32 lv = (u32)m0, dl = (u32)(m0 >> 32), dh = s0 ? (u32)mc[s_ * 4 + 1] : dha;
+                    if (lv > 0 && dh >= b1) m = b1 <= dl ? lv : dirv(s_, dh - b1);
+                }
+                const u32 incl = wave_incl_scan(m);
+                if (s_ < S) sm.seg_count[s_] = carry + incl - m;
+                carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+            }
+            if (l == 0) {
+                sm.loc_digit[0] = b1;
+                sm.loc_r[0] = r1;
+                sm.loc_c[0] = c1;
+                sm.newtotal = carry;
+            }
+        }
+        __syncthreads();
+
+        b1 = sm.loc_digit[0];
+        r1 = sm.loc_r[0];
+        c1 = sm.loc_c[0];
+        total = sm.newtotal;
     }
-    __syncthreads();
-    const u32 b1 = sm.loc_digit[0], r1 = sm.loc_r[0], c1 = sm.loc_c[0], total = sm.newtotal;
     DSTK_T(sm, kPhLoad);
     if (total > (u32)CAP) {
+        if (direct) __syncthreads();  // (mc and dc are still being read)
         merge_fallback<E, WG, CAP>(sm, ws_meta + (u64)row * S * 4, rdir, rc, S, cap, digit_floor(b1), k, n,
                                    sorted, retval,
                                    flags, row_idx.p, row_val, flag, flag_value);
@@ -2824,22 +2908,11 @@ __device__ __forceinline__ void topk_rows_body(const Params& p) {
     // pass over the buffer afterwards.
     u64 fo = 0, fa = ~0ull;  // OR / AND of this thread's entries of bin b1
     {
-        // G threads per segment load its share (no search for the source)
-        const u32 G = (u32)WG / S;  // (S <= 256: two or more)
-        const u32 s_ = tid / G, j0 = tid - s_ * G;
-        const u32 off = s_ < S ? sm.seg_count[s_] : 0u;
-        const u32 share = s_ < S ? (s_ + 1 < S ? sm.seg_count[s_ + 1] : total) - off : 0u;
-        const gptr<const u64> src = rc + (u64)(s_ < S ? s_ : 0u) * cap;
-        constexpr int kLB = 4;  // loads in flight per thread
-        u64 v[kLB];
-        auto load = [&](u32 j) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < kLB; ++u) {
-                const u32 jj = j + (u32)u * G;
-                v[u] = jj < share ? ld_agent(&src[jj]) : 0ull;
-            }
-        };
-        load(j0);  // (in flight while the histogram is cleared)
+        // G threads per segment load its share (no search for the source);
+        // the first loads are in flight since the metadata arrived
+        const u32 s_ = ls, j0 = lj0;
+        const u32 off = direct ? d_off : s_ < S ? sm.seg_count[s_] : 0u;
+        const u32 share = direct ? d_share : s_ < S ? (s_ + 1 < S ? sm.seg_count[s_ + 1] : total) - off : 0u;
         for (u32 i = tid; i < (u32)kHistWords; i += WG) sm.hist[i] = 0;  // zero for the selection
         __syncthreads();
         const FirstLevel<kFirstOf<E>, CAP> fl(sm, total, col_bits(n));
@@ -2852,7 +2925,7 @@ __device__ __forceinline__ void topk_rows_body(const Params& p) {
                     if (top_digit(v[u]) == b1) fl.add(sm, v[u], off + jj, fo, fa);
                 }
             }
-            if (j + G * kLB < share) load(j + G * kLB);
+            if (j + G * kLB < share) load(j + G * kLB, share);
         }
     }
     __syncthreads();
