@@ -15,7 +15,10 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ds_topk.hip")
 # the selection with its sampling step, compiled as a unit of its own
 SAMPLE_SRC = os.path.join(HERE, "csrc", "sample_fused.hip")
-DEPS = [SRC, SAMPLE_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
+# the 16384-entry instances, a unit of their own with their own scheduling option
+BIGK_SRC = os.path.join(HERE, "csrc", "bigk.hip")
+BIGK_FLAGS = ("-mllvm", "-amdgpu-use-amdgpu-trackers")
+DEPS = [SRC, SAMPLE_SRC, BIGK_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
         os.path.join(ROOT, "include", "ds_topk.h")]
 LIB = os.path.join(HERE, "libds_topk.so")
 # Measurement build of the same sources: the kernels also note phase
@@ -27,7 +30,7 @@ CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Files whose content decides the top-k kernels' code (for tagging profiles).
-KERNEL_SOURCES = (SRC, SAMPLE_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"),
+KERNEL_SOURCES = (SRC, SAMPLE_SRC, BIGK_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"),
                   os.path.join(ROOT, "include", "ds_topk.h"), os.path.abspath(__file__))
 
 
@@ -69,17 +72,37 @@ def stale(lib: str = LIB, deps=None) -> bool:
     return any(os.path.getmtime(d) > t for d in deps)
 
 
-def _hipcc(src, lib: str, verbose: bool, extra=()) -> None:
-    tmp = lib + ".tmp%d" % os.getpid()
-    srcs = [src] if isinstance(src, str) else list(src)
-    cmd = [HIPCC] + FLAGS + list(extra) + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-                                           "-o", tmp] + srcs
+def _run(cmd, verbose: bool) -> None:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
+
+
+def _hipcc(src, lib: str, verbose: bool, extra=()) -> None:
+    """Compile and link `src` (a path, or a list of paths and (path, flags)
+    pairs whose flags apply to that unit only) into the shared library `lib`."""
+    tmp = lib + ".tmp%d" % os.getpid()
+    srcs = [src] if isinstance(src, str) else list(src)
+    units = [(s, ()) if isinstance(s, str) else (s[0], tuple(s[1])) for s in srcs]
+    base = [HIPCC] + FLAGS + list(extra) + ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    if all(not f for _, f in units):
+        _run(base + ["-o", tmp] + [s for s, _ in units], verbose)
+    else:
+        # one object per unit (each with its own device code), then one link
+        objs = []
+        try:
+            for i, (s, f) in enumerate(units):
+                o = "%s.%d.o" % (tmp, i)
+                _run([a for a in base if a != "-shared"] + list(f) + ["-c", "-o", o, s], verbose)
+                objs.append(o)
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        finally:
+            for o in objs:
+                if os.path.exists(o):
+                    os.remove(o)
     os.replace(tmp, lib)
 
 
@@ -88,11 +111,11 @@ def build(force: bool = True, verbose: bool = False, timing: bool = True) -> str
     calibration kernels) and, with `timing`, libds_topk_timing.so (the
     library with phase timestamps, for measurement only)."""
     if force or stale():
-        _hipcc([SRC, SAMPLE_SRC], LIB, verbose)
+        _hipcc([SRC, SAMPLE_SRC, (BIGK_SRC, BIGK_FLAGS)], LIB, verbose)
     if force or stale(CALIB_LIB, [CALIB_SRC]):
         _hipcc(CALIB_SRC, CALIB_LIB, verbose)
     if timing and (force or stale(TIMING_LIB)):
-        _hipcc([SRC, SAMPLE_SRC], TIMING_LIB, verbose, ["-DDSTK_TIMING"])
+        _hipcc([SRC, SAMPLE_SRC, (BIGK_SRC, BIGK_FLAGS)], TIMING_LIB, verbose, ["-DDSTK_TIMING"])
     return LIB
 
 

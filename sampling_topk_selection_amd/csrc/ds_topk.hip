@@ -287,6 +287,9 @@ hipError_t launch_one(const dstk::Params& prm, int64_t grid, hipStream_t s) {
 // of its own, so the selection kernels here share no out-of-line function
 // with it and keep their own register allocation).
 hipError_t ds_topk_launch_sample_fused(int eb, const dstk::Params& prm, int64_t grid, hipStream_t s);
+// The selection with the 16384-entry buffer (bigk.hip: a unit of its own,
+// built with other scheduling options).
+hipError_t ds_topk_launch_bigk(int eb, const dstk::Params& prm, int64_t grid, hipStream_t s);
 
 namespace {
 
@@ -296,12 +299,9 @@ namespace {
 hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStream_t s, bool sample = false) {
     const int64_t grid = rows * pl.segs;
     if (sample) return ds_topk_launch_sample_fused(pl.eb, prm, grid, s);  // (sampling_fused: capacity 8192)
-    if (pl.eb == 4) {
-        if (pl.cap == 8192) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
-        return launch_one<4, 512, kChunkF32, 16384>(prm, grid, s);
-    }
-    if (pl.cap == 8192) return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
-    return launch_one<2, 512, kChunkBf16BigK, 16384>(prm, grid, s);
+    if (pl.cap != 8192) return ds_topk_launch_bigk(pl.eb, prm, grid, s);
+    if (pl.eb == 4) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
+    return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
 }
 
 // Per-row sampling inputs and the token output, for a selection that draws
