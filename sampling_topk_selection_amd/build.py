@@ -18,8 +18,13 @@ SAMPLE_SRC = os.path.join(HERE, "csrc", "sample_fused.hip")
 # the 16384-entry instances, a unit of their own with their own scheduling option
 BIGK_SRC = os.path.join(HERE, "csrc", "bigk.hip")
 BIGK_FLAGS = ("-mllvm", "-amdgpu-use-amdgpu-trackers")
-DEPS = [SRC, SAMPLE_SRC, BIGK_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
+# the bf16 8192-entry instance, likewise
+BF16_SRC = os.path.join(HERE, "csrc", "rows_bf16.hip")
+BF16_FLAGS = ("-mllvm", "-structurizecfg-skip-uniform-regions")
+DEPS = [SRC, SAMPLE_SRC, BIGK_SRC, BF16_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"), os.path.join(HERE, "csrc", "sample_kernels.hpp"),
         os.path.join(ROOT, "include", "ds_topk.h")]
+# the library's compilation units, with the flags each adds
+UNITS = [SRC, SAMPLE_SRC, (BIGK_SRC, BIGK_FLAGS), (BF16_SRC, BF16_FLAGS)]
 LIB = os.path.join(HERE, "libds_topk.so")
 # Measurement build of the same sources: the kernels also note phase
 # timestamps (DSTK_TIMING); read by sampling_topk_selection_amd.phases.
@@ -30,7 +35,7 @@ CALIB_LIB = os.path.join(HERE, "libds_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Files whose content decides the top-k kernels' code (for tagging profiles).
-KERNEL_SOURCES = (SRC, SAMPLE_SRC, BIGK_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"),
+KERNEL_SOURCES = (SRC, SAMPLE_SRC, BIGK_SRC, BF16_SRC, os.path.join(HERE, "csrc", "topk_kernels.hpp"),
                   os.path.join(ROOT, "include", "ds_topk.h"), os.path.abspath(__file__))
 
 
@@ -111,11 +116,11 @@ def build(force: bool = True, verbose: bool = False, timing: bool = True) -> str
     calibration kernels) and, with `timing`, libds_topk_timing.so (the
     library with phase timestamps, for measurement only)."""
     if force or stale():
-        _hipcc([SRC, SAMPLE_SRC, (BIGK_SRC, BIGK_FLAGS)], LIB, verbose)
+        _hipcc(UNITS, LIB, verbose)
     if force or stale(CALIB_LIB, [CALIB_SRC]):
         _hipcc(CALIB_SRC, CALIB_LIB, verbose)
     if timing and (force or stale(TIMING_LIB)):
-        _hipcc([SRC, SAMPLE_SRC, (BIGK_SRC, BIGK_FLAGS)], TIMING_LIB, verbose, ["-DDSTK_TIMING"])
+        _hipcc(UNITS, TIMING_LIB, verbose, ["-DDSTK_TIMING"])
     return LIB
 
 

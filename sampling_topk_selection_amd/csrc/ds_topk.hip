@@ -290,6 +290,8 @@ hipError_t ds_topk_launch_sample_fused(int eb, const dstk::Params& prm, int64_t 
 // The selection with the 16384-entry buffer (bigk.hip: a unit of its own,
 // built with other scheduling options).
 hipError_t ds_topk_launch_bigk(int eb, const dstk::Params& prm, int64_t grid, hipStream_t s);
+// The bf16 selection with the 8192-entry buffer (rows_bf16.hip, likewise).
+hipError_t ds_topk_launch_bf16(const dstk::Params& prm, int64_t grid, hipStream_t s);
 
 namespace {
 
@@ -301,7 +303,7 @@ hipError_t launch(const Plan& pl, const dstk::Params& prm, int64_t rows, hipStre
     if (sample) return ds_topk_launch_sample_fused(pl.eb, prm, grid, s);  // (sampling_fused: capacity 8192)
     if (pl.cap != 8192) return ds_topk_launch_bigk(pl.eb, prm, grid, s);
     if (pl.eb == 4) return launch_one<4, 512, kChunkF32, 8192>(prm, grid, s);
-    return launch_one<2, 512, kChunkBf16, 8192>(prm, grid, s);
+    return ds_topk_launch_bf16(prm, grid, s);
 }
 
 // Per-row sampling inputs and the token output, for a selection that draws

@@ -1,6 +1,6 @@
 """CPU: the oracle (oracle/oracle.c) and the host half of the library
 (argument checks, planning, the no-alloc size check; the host code of
-ds_topk.hip, sample_fused.hip and bigk.hip) built with AddressSanitizer and UndefinedBehaviorSanitizer and driven
+ds_topk.hip and the units beside it) built with AddressSanitizer and UndefinedBehaviorSanitizer and driven
 through their entry points by small C/C++ drivers, which also check the
 results they can check without a GPU.  Any sanitizer report fails the run
 (-fno-sanitize-recover).  The device code of ds_topk.hip is compiled as usual
@@ -50,6 +50,7 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
             os.path.join(ROOT, "sampling_topk_selection_amd", "csrc", "ds_topk.hip"),
             os.path.join(ROOT, "sampling_topk_selection_amd", "csrc", "sample_fused.hip"),
             os.path.join(ROOT, "sampling_topk_selection_amd", "csrc", "bigk.hip"),
+            os.path.join(ROOT, "sampling_topk_selection_amd", "csrc", "rows_bf16.hip"),
             os.path.join(HERE, "asan_host_driver.cpp"), "-o", exe])
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
