@@ -42,6 +42,25 @@ def test_library_exports_every_declared_symbol(pkg):
     assert set(pkg.EXPORTS) == set(declared_functions())
 
 
+def test_every_kernel_unit_is_built():
+    # the library is linked from several compilation units (each with its own
+    # scheduling options): every HIP source beside ds_topk.hip is one of them,
+    # and every launcher ds_topk.hip declares is defined in one
+    from sampling_topk_selection_amd import build as b
+
+    csrc = os.path.join(ROOT, "sampling_topk_selection_amd", "csrc")
+    units = {os.path.abspath(u if isinstance(u, str) else u[0]) for u in b.UNITS}
+    hips = {os.path.abspath(os.path.join(csrc, f)) for f in os.listdir(csrc) if f.endswith(".hip")}
+    assert units == hips - {os.path.abspath(b.CALIB_SRC)}
+    main = open(b.SRC).read()
+    launchers = set(re.findall(r"^hipError_t (ds_topk_launch_\w+)\(", main, flags=re.M))
+    assert launchers
+    others = "".join(open(u).read() for u in units if u != os.path.abspath(b.SRC))
+    for name in launchers:
+        assert re.search(r"^hipError_t %s\(.*\{" % name, others, flags=re.M), name
+    assert set(b.KERNEL_SOURCES) >= units and set(b.DEPS) >= units
+
+
 def test_binds_to_one_hip_runtime(pkg):
     maps = open("/proc/self/maps").read()
     libs = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
